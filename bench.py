@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the LM-head hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input,
+M=1024 tokens, K=8192 hidden, V=32768 vocabulary (x ~ N(0,1),
+W ~ N(0, 0.02^2), BF16):
+
+    lmhead_logits (FP32 out) -> lmhead_xent_fwd -> lmhead_xent_mean
+    -> lmhead_xent_bwd (BF16 dlogits) -> lmhead_dgrad -> lmhead_wgrad
+
+W warmup steps, then K timed steps bracketed by torch.cuda.synchronize();
+HIP events on the launch stream give each kernel's duration.  `value` is the
+logits GEMM's TFLOPS (2*M*K*V per launch / mean launch time) -- the first
+half of the metric.  Beside the step the same run measures:
+
+* the FP32-output vs BF16-output logits GEMM, the pages' protocol
+  (preallocated outputs, 10 warmup pairs, 30 alternating samples, medians;
+  Megatron-LM "Add mixed-precision (FP32) LM output logits", section "GEMM
+  kernel benchmark");
+* the fused CE forward + FP32 backward over FP32 logits [8192 x 131072]
+  (N(0, 3^2), 1% rows +30 spikes, 2% ignored) -- the second half of the
+  metric, in GB/s of algorithmic bytes -- out of place, in place and with
+  BF16 gradients;
+* the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LM-head GEMM TFLOPS (% MFMA peak) + fused CE fwd+bwd GB/s (% HBM peak)"
+# MI355X published dense peaks: BF16 MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz;
+# HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--samples", type=int, default=30, help="samples per side measurement")
+    ap.add_argument("--ce-rows", type=int, default=8192, help="rows of the large CE workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true", help="skip the side measurements")
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """Start/end HIP events around each named launch on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def __call__(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+        return r
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
+
+def dev_bf16(torch, np, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU layout is described in the design notes, not built.", flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import lm_head_fp32_amd as lmh
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lmh.lib()
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+
+    # ------------------------------------------------------------ the step
+    M, K, V = 1024, 8192, 32768
+    log(f"[bench] generating lmhead_1024 inputs M={M} K={K} V={V}")
+    inp = workloads.lmhead_1024()
+    x = dev_bf16(torch, np, inp.x)
+    W = dev_bf16(torch, np, inp.W)
+    tgt = torch.from_numpy(inp.target).cuda()
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    logits_b = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+    loss = torch.empty((M,), dtype=torch.float32, device="cuda")
+    stats = torch.empty((M, 4), dtype=torch.float32, device="cuda")
+    mean = torch.empty((1,), dtype=torch.float32, device="cuda")
+    inv = torch.empty((1,), dtype=torch.float32, device="cuda")
+    dlog = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((V, K), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(tm):
+        tm("logits", lambda: lmh.lmhead_logits(x, W, out=logits, out_dtype="fp32"))
+        tm("xent_fwd", lambda: lmh.lmhead_xent_fwd(logits, tgt, -100, loss=loss, stats=stats))
+        tm("xent_mean", lambda: lmh.lmhead_xent_mean(loss, tgt, -100, mean=mean, inv_nvalid=inv))
+        tm("xent_bwd", lambda: lmh.lmhead_xent_bwd(logits, stats, tgt, inv, -100, dlogits=dlog,
+                                                   grad_dtype="bf16"))
+        tm("dgrad", lambda: lmh.lmhead_dgrad(dlog, W, dX=dX, dx_dtype="bf16"))
+        tm("wgrad", lambda: lmh.lmhead_wgrad(dlog, x, dW=dW))
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(KernelTimer(torch))
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    tm = KernelTimer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / max(args.steps, 1)
+
+    flop = 2.0 * M * K * V
+    kern = {}
+    for name in ("logits", "xent_fwd", "xent_mean", "xent_bwd", "dgrad", "wgrad"):
+        ts = tm.ms(name)
+        kern[name] = {"ms_mean": statistics.fmean(ts), "ms_median": statistics.median(ts),
+                      "ms_min": min(ts)}
+    for name in ("logits", "dgrad", "wgrad"):
+        kern[name]["tflops"] = flop / (kern[name]["ms_mean"] * 1e-3) / 1e12
+        kern[name]["frac_mfma_peak"] = kern[name]["tflops"] / PEAK_BF16_TFLOPS
+    ce_step_bytes = (4.0 * M * V + 24 * M) + ((4.0 + 2.0) * M * V + 24 * M)
+    ce_step_ms = kern["xent_fwd"]["ms_mean"] + kern["xent_bwd"]["ms_mean"]
+    kern["xent_fwd_bwd_bf16"] = {"gbps": ce_step_bytes / (ce_step_ms * 1e-3) / 1e9,
+                                 "note": "logits (128 MiB) may sit in the 256 MB MALL here"}
+    logits_tflops = kern["logits"]["tflops"]
+    log(f"[bench] step {ms_step:.3f} ms; logits {kern['logits']['ms_mean']:.3f} ms "
+        f"= {logits_tflops:.1f} TFLOPS")
+
+    out = {
+        "metric": METRIC,
+        "value": round(logits_tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "lm-head step M=1024 K=8192 V=32768: fp32 logits -> CE fwd -> mean -> "
+                        "CE bwd (bf16 dlogits) -> dgrad -> wgrad; plus CE fwd+bwd on fp32 "
+                        "logits 8192x131072",
+            "M": M, "K": K, "V": V, "global_batch": M, "parallelism": "none (1 GPU)",
+            "device": dev_name,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "lmhead_logits (fp32 out)",
+            "achieved": round(logits_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(logits_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "kernels": kern,
+    }
+
+    # ----------------------------------------------------- side measurements
+    if not args.no_side:
+        # FP32 vs BF16 epilogue, the pages' protocol
+        log("[bench] fp32-out vs bf16-out logits, 10 warmup pairs + alternating samples")
+        for _ in range(10):
+            lmh.lmhead_logits(x, W, out=logits, out_dtype="fp32")
+            lmh.lmhead_logits(x, W, out=logits_b, out_dtype="bf16")
+        side = KernelTimer(torch)
+        for i in range(args.samples):
+            order = ("fp32", "bf16") if i % 2 == 0 else ("bf16", "fp32")
+            for o in order:
+                side(o, lambda o=o: lmh.lmhead_logits(x, W, out=logits if o == "fp32" else logits_b,
+                                                       out_dtype=o))
+        torch.cuda.synchronize()
+        f32 = statistics.median(side.ms("fp32"))
+        b16 = statistics.median(side.ms("bf16"))
+        out["logits_fp32_vs_bf16"] = {
+            "fp32_ms_median": f32, "bf16_ms_median": b16,
+            "fp32_tflops": flop / (f32 * 1e-3) / 1e12, "bf16_tflops": flop / (b16 * 1e-3) / 1e12,
+            "fp32_overhead_pct": 100.0 * (f32 / b16 - 1.0),
+        }
+        del logits_b
+        # Large-vocabulary CE
+        n_ce, v_ce = args.ce_rows, 131072
+        log(f"[bench] generating CE logits {n_ce}x{v_ce}")
+        ce = workloads.xent_logits(n_ce, v_ce, sigma=3.0, spike_frac=0.01, spike=30.0,
+                                   ignore_frac=0.02, seed=workloads.SEED)
+        z = torch.from_numpy(ce.logits).cuda()
+        ct = torch.from_numpy(ce.target).cuda()
+        del ce
+        cl = torch.empty((n_ce,), dtype=torch.float32, device="cuda")
+        cs = torch.empty((n_ce, 4), dtype=torch.float32, device="cuda")
+        cm = torch.empty((1,), dtype=torch.float32, device="cuda")
+        ci = torch.empty((1,), dtype=torch.float32, device="cuda")
+        g32 = torch.empty((n_ce, v_ce), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        log("[bench] CE fwd + bwd samples")
+        for _ in range(3):
+            lmh.lmhead_xent_fwd(z, ct, -100, loss=cl, stats=cs)
+            lmh.lmhead_xent_mean(cl, ct, -100, mean=cm, inv_nvalid=ci)
+            lmh.lmhead_xent_bwd(z, cs, ct, ci, -100, dlogits=g32)
+        ctm = KernelTimer(torch)
+        for _ in range(args.samples):
+            ctm("fwd", lambda: lmh.lmhead_xent_fwd(z, ct, -100, loss=cl, stats=cs))
+            lmh.lmhead_xent_mean(cl, ct, -100, mean=cm, inv_nvalid=ci)
+            ctm("bwd", lambda: lmh.lmhead_xent_bwd(z, cs, ct, ci, -100, dlogits=g32))
+        torch.cuda.synchronize()
+        fwd_ms = statistics.median(ctm.ms("fwd"))
+        bwd_ms = statistics.median(ctm.ms("bwd"))
+        fwd_b = 4.0 * n_ce * v_ce + 24 * n_ce
+        bwd_b = 8.0 * n_ce * v_ce + 24 * n_ce
+        ce_gbps = (fwd_b + bwd_b) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9
+        # BF16 gradients, then in place over a copy restored outside the timing
+        gb = torch.empty((n_ce, v_ce), dtype=torch.bfloat16, device="cuda")
+        for _ in range(2):
+            lmh.lmhead_xent_bwd(z, cs, ct, ci, -100, dlogits=gb, grad_dtype="bf16")
+        for _ in range(args.samples):
+            ctm("bwd_bf16", lambda: lmh.lmhead_xent_bwd(z, cs, ct, ci, -100, dlogits=gb,
+                                                        grad_dtype="bf16"))
+        torch.cuda.synchronize()
+        del gb
+        bwd16_ms = statistics.median(ctm.ms("bwd_bf16"))
+        n_inplace = min(args.samples, 10)
+        for _ in range(n_inplace):
+            g32.copy_(z)  # restore pristine logits, outside the timed events
+            ctm("bwd_inplace", lambda: lmh.lmhead_xent_bwd(g32, cs, ct, ci, -100, in_place=True))
+        torch.cuda.synchronize()
+        bwdip_ms = statistics.median(ctm.ms("bwd_inplace"))
+        out["roofline_ce"] = {
+            "bound": "hbm",
+            "kernel": "lmhead_xent_fwd + lmhead_xent_bwd (fp32 grads, out of place)",
+            "workload": f"fp32 logits {n_ce}x{v_ce}",
+            "achieved": round(ce_gbps, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(ce_gbps / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "fwd_ms_median": fwd_ms, "bwd_ms_median": bwd_ms,
+            "fwd_gbps": fwd_b / (fwd_ms * 1e-3) / 1e9, "bwd_gbps": bwd_b / (bwd_ms * 1e-3) / 1e9,
+            "bwd_bf16_ms_median": bwd16_ms,
+            "bwd_bf16_gbps": (6.0 * n_ce * v_ce + 24 * n_ce) / (bwd16_ms * 1e-3) / 1e9,
+            "bwd_inplace_ms_median": bwdip_ms,
+            "bwd_inplace_gbps": bwd_b / (bwdip_ms * 1e-3) / 1e9,
+        }
+        log(f"[bench] CE fwd {fwd_ms:.3f} ms bwd {bwd_ms:.3f} ms -> {ce_gbps:.0f} GB/s")
+        del z, g32
+
+    # ------------------------------------------------------- CPU baseline
+    if not args.no_cpu_baseline:
+        import oracle
+
+        thr = oracle.default_threads()
+        rows = np.arange(0, M, max(1, M // (4 * thr)))[: 4 * thr]
+        log(f"[bench] cpu baseline: oracle logits on {rows.size} of {M} rows, {thr} threads")
+        t0 = time.perf_counter()
+        oracle.logits(inp.x, inp.W, rows=rows, with_abs=False, nthreads=thr)
+        dt = time.perf_counter() - t0
+        cpu_tflops = 2.0 * rows.size * K * V / dt / 1e12
+        n_cpu = 4 * thr
+        ce = workloads.xent_logits(n_cpu, 131072, sigma=3.0, spike_frac=0.01, spike=30.0,
+                                   ignore_frac=0.02, seed=workloads.SEED)
+        t0 = time.perf_counter()
+        st = oracle.xent_fwd(ce.logits, ce.target, -100, nthreads=thr)
+        _, inv_ref, _ = oracle.xent_mean(st[:, 3], ce.target, -100)
+        oracle.xent_bwd(ce.logits, ce.target, -100, inv_ref, nthreads=thr)
+        dtc = time.perf_counter() - t0
+        cpu_ce = (12.0 * n_cpu * 131072 + 48 * n_cpu) / dtc / 1e9
+        out["cpu_baseline"] = {
+            "value": round(cpu_tflops, 6), "unit": "TFLOPS", "cores": thr, "kind": "oracle",
+            "sample": f"FP64 oracle logits GEMM on {rows.size} of {M} rows (K={K}, V={V}), "
+                      f"{dt:.2f} s; CE fwd+bwd on {n_cpu} rows x 131072, {dtc:.2f} s",
+            "ce_gbps": round(cpu_ce, 4),
+        }
+        log(f"[bench] cpu baseline {cpu_tflops * 1e3:.2f} GFLOPS, CE {cpu_ce:.3f} GB/s")
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

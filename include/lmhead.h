@@ -1,0 +1,185 @@
+/*
+ * lmhead.h -- C ABI of liblmhead.so: the LM output layer with FP32 logits and
+ * a fused FP32 vocabulary cross-entropy, hand-written HIP for gfx950 (MI355X).
+ *
+ * Sources the operations follow (cited by page title and section):
+ *  [MIXED] Megatron-LM pull request "Add mixed-precision (FP32) LM output
+ *          logits": section "What does this PR do?" (the output-layer GEMM
+ *          keeps its FP32 accumulator as FP32 logits instead of rounding each
+ *          logit to BF16; the backward casts the logits gradient to BF16 for
+ *          the GEMMs that follow) and section "Tests" (the logit dtype option
+ *          accepts bf16 and fp32 and rejects fp16).
+ *  [XENT]  Transformer Engine issue "[Pytorch] change fused cross entropy
+ *          backward grad to fp32 and reduce one read/...": sections
+ *          "Description" and "Changes" (the backward gradient is computed in
+ *          FP32; one logits read is removed) and the discussion (the forward
+ *          keeps the input, an n_rows x 1 target and an n_rows x 4 m_d_X_y
+ *          record; the original kernel wrote the gradient over its input).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device.  The
+ *    caller owns every buffer; the library allocates nothing and keeps no
+ *    state between calls.  Calls are thread-safe.
+ *  - Matrices are row-major with a leading dimension `ld*` in ELEMENTS
+ *    (row r starts at base + r * ld).  BF16 tensors are raw 16-bit words
+ *    (the top half of an IEEE binary32).
+ *  - Every call validates its arguments on the host first and returns a
+ *    non-zero LMH_ERR_* code WITHOUT touching the GPU when they are invalid.
+ *    Otherwise it enqueues its kernels on `stream` (a hipStream_t passed as
+ *    void*, NULL = the default stream) and returns at once; LMH_ERR_LAUNCH
+ *    reports a failed launch.  Results are ready when the stream reaches
+ *    that point.
+ *  - Alignment: every pointer 16-byte aligned; `ld` a multiple of 8 for BF16
+ *    and of 4 for FP32 (LMH_ERR_ALIGN).  ld must be >= the row length
+ *    (LMH_ERR_SHAPE).  Sizes are >= 0; a zero-size output is a no-op.
+ *  - Padding between a row's end and the next row (ld > row length) is never
+ *    written.
+ *  - Results are bitwise deterministic run to run; no kernel uses floating
+ *    point atomics.
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  LMH_FP16 exists only so that it can be rejected ([MIXED],
+ * "Tests": the logit dtype accepts bf16 and fp32 and rejects fp16). */
+enum lmh_dtype { LMH_BF16 = 0, LMH_FP32 = 1, LMH_FP16 = 2 };
+
+enum lmh_status {
+    LMH_OK = 0,
+    LMH_ERR_DTYPE = 1,  /* unsupported element type (fp16 or unknown)        */
+    LMH_ERR_SHAPE = 2,  /* negative size, ld too small, bad stride or limit  */
+    LMH_ERR_NULL = 3,   /* required pointer is NULL                          */
+    LMH_ERR_ALIGN = 4,  /* pointer not 16-B aligned or ld not a multiple     */
+    LMH_ERR_ALIAS = 5,  /* an output overlaps an input in an unsupported way */
+    LMH_ERR_LAUNCH = 6  /* the HIP launch failed (see hipGetLastError)       */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *lmhead_status_str(int32_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t lmhead_version(void);
+
+/*
+ * lmhead_logits -- logits[M x V] = x[M x K] . W[V x K]^T        ([MIXED])
+ *
+ *  x    BF16 activations, row-major [M x K], leading dimension ldx >= K.
+ *  W    BF16 vocabulary weights, row-major [V x K] (K contiguous), ldw >= K.
+ *  out  logits, row-major [M x V], ldo >= V, element type out_dtype:
+ *         LMH_FP32 -- the FP32 MFMA accumulator stored as is (the new path);
+ *         LMH_BF16 -- the same accumulator rounded to BF16, nearest-even (the
+ *                     legacy path kept for comparison);
+ *         LMH_FP16 or anything else -- LMH_ERR_DTYPE.
+ *  Products of BF16 values are exact in FP32 and every sum is FP32; with
+ *  integer operands whose partial sums stay below 2^24 the FP32 result is
+ *  exact, independent of summation order.  K == 0 writes zeros.
+ *  `out` must not overlap x or W (LMH_ERR_ALIAS).
+ */
+int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw,
+                      void *out, int64_t ldo, int32_t out_dtype,
+                      int64_t M, int64_t K, int64_t V, void *stream);
+
+/*
+ * lmhead_xent_fwd -- fused cross-entropy forward over FP32 logits  ([XENT])
+ *
+ *  logits  FP32 [n_rows x n_cols], leading dimension ld >= n_cols; read once.
+ *  target  int32 [n_rows]; a row whose target equals ignore_index is ignored.
+ *  loss    FP32 [n_rows] per-row loss, or NULL to skip it.
+ *  stats   FP32 [n_rows x 4], one 16-byte record per row:
+ *            stats[i] = { m_i   = max_j z_ij,
+ *                         d_i   = sum_j exp(z_ij - m_i),
+ *                         X_i   = z_i,target_i,
+ *                         loss_i = (m_i - X_i) + log d_i }.
+ *          An ignored row stores {m_i, d_i, 0, 0} and loss 0.  A target that is
+ *          neither ignore_index nor in [0, n_cols) cannot be reported from the
+ *          kernel: that row stores X = NaN and loss = NaN.
+ *  n_cols >= 1 when n_rows > 0.  stats and loss must not overlap the logits.
+ */
+int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                        const int32_t *target, int32_t ignore_index,
+                        float *loss, float *stats, void *stream);
+
+/*
+ * lmhead_xent_mean -- mean reduction of the per-row loss
+ *
+ *  loss     FP32 [n_rows]; target int32 [n_rows] (rows equal to ignore_index
+ *           are excluded).
+ *  mean_out FP32 scalar: sum of valid losses / n_valid (0 if n_valid == 0),
+ *           or NULL.
+ *  inv_nvalid_out FP32 scalar: 1 / n_valid (0 if n_valid == 0), or NULL; it is
+ *           the upstream gradient of every row of a mean loss and can be passed
+ *           to lmhead_xent_bwd as `dloss` with dloss_stride 0.
+ *  One workgroup sums in a fixed order (FP64), so the result is
+ *  deterministic.  Both outputs NULL is a no-op.
+ */
+int32_t lmhead_xent_mean(const float *loss, const int32_t *target, int32_t ignore_index,
+                         int64_t n_rows, float *mean_out, float *inv_nvalid_out,
+                         void *stream);
+
+/*
+ * lmhead_xent_bwd -- fused cross-entropy backward in FP32          ([XENT])
+ *
+ *  dlogits_ij = dloss_i * (exp(z_ij - m_i) / d_i - [j == target_i]),
+ *  computed in FP32 from the logits (read once more) and the stats record of
+ *  lmhead_xent_fwd; rows whose target is ignore_index get zeros.
+ *
+ *  logits   FP32 [n_rows x n_cols], leading dimension ld.
+ *  stats    FP32 [n_rows x 4] from lmhead_xent_fwd (m and d are used).
+ *  target   int32 [n_rows]; ignore_index as in the forward.
+ *  dloss    FP32 device pointer: dloss_i = dloss[dloss_stride * i] with
+ *           dloss_stride 0 (one scalar for every row, e.g. the inv_nvalid
+ *           output of lmhead_xent_mean) or 1 (one value per row).
+ *  dlogits  [n_rows x n_cols], leading dimension ldg, type grad_dtype:
+ *             LMH_FP32 -- FP32 gradient;
+ *             LMH_BF16 -- the same FP32 value rounded to BF16 (nearest-even),
+ *                         the cast the backward applies before the GEMMs
+ *                         ([MIXED]);
+ *           In place: dlogits == logits with ldg == ld and LMH_FP32 writes the
+ *           gradient over the logits (each element is read, then overwritten
+ *           by the same thread).  Any other overlap with logits, stats, target
+ *           or dloss, or BF16 in place, is LMH_ERR_ALIAS.
+ *  A target outside [0, n_cols) that is not ignore_index yields a NaN row.
+ */
+int32_t lmhead_xent_bwd(const float *logits, int64_t ld, const float *stats,
+                        const int32_t *target, int32_t ignore_index,
+                        const float *dloss, int64_t dloss_stride,
+                        void *dlogits, int64_t ldg, int32_t grad_dtype,
+                        int64_t n_rows, int64_t n_cols, void *stream);
+
+/*
+ * lmhead_dgrad -- input gradient dX[M x K] = dlogits[M x V] . W[V x K]
+ *
+ *  The GEMM that consumes the BF16 logits gradient ([MIXED]: the backward
+ *  casts the gradient to BF16 for the following GEMMs).
+ *  dlogits BF16 [M x V], ldd >= V;  W BF16 [V x K], ldw >= K;
+ *  dX [M x K], ldx >= K, dx_dtype LMH_BF16 (nearest-even) or LMH_FP32.
+ *  FP32 accumulation; V == 0 writes zeros.  dX must not overlap the inputs.
+ */
+int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ldw,
+                     void *dX, int64_t ldx, int32_t dx_dtype,
+                     int64_t M, int64_t K, int64_t V, void *stream);
+
+/*
+ * lmhead_wgrad -- weight gradient dW[V x K] (+)= dlogits[M x V]^T . x[M x K]
+ *
+ *  dlogits BF16 [M x V], ldd >= V;  x BF16 [M x K], ldx >= K;
+ *  dW FP32 [V x K], ldw >= K.  accumulate == 0 overwrites dW; accumulate != 0
+ *  adds the product to the FP32 values already in dW.  FP32 accumulation over
+ *  M; M == 0 writes zeros (or leaves dW unchanged when accumulating).
+ *  dW must not overlap the inputs.
+ */
+int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ldx,
+                     float *dW, int64_t ldw, int32_t accumulate,
+                     int64_t M, int64_t K, int64_t V, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

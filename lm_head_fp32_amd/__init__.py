@@ -1,0 +1,271 @@
+"""lm_head_fp32_amd -- FP32 LM-head logits and fused FP32 cross-entropy on
+MI355X (gfx950), as a thin Python binding over ``liblmhead.so``.
+
+Every function here has the name of the C entry point it calls (see
+``include/lmhead.h``) and only marshals arguments: checks that tensors are
+on the GPU with the right dtype, reads pointers, leading dimensions and the
+current stream, allocates outputs the caller did not pass, and raises
+``LmheadError`` on a non-zero status.  All arithmetic runs in the HIP
+kernels.  There is no fallback: without the built library every call raises.
+
+Shapes (row-major, last dimension contiguous, rows may be padded):
+  x [M, K] bf16, W [V, K] bf16 -> logits [M, V] fp32 or bf16
+  logits [n, V] fp32, target [n] int32 -> loss [n] fp32, stats [n, 4] fp32
+  stats {m, d, X_y, loss} per row; dlogits [n, V] fp32 or bf16
+  dgrad: dlogits [M, V] bf16, W [V, K] bf16 -> dX [M, K]
+  wgrad: dlogits [M, V] bf16, x [M, K] bf16 -> dW [V, K] fp32
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LMH_BF16", "LMH_FP32", "LMH_FP16", "STATS_COLS", "LmheadError", "lib", "library_path",
+    "lmhead_logits", "lmhead_xent_fwd", "lmhead_xent_mean", "lmhead_xent_bwd",
+    "lmhead_dgrad", "lmhead_wgrad", "lmhead_status_str", "lmhead_version",
+]
+
+LMH_BF16, LMH_FP32, LMH_FP16 = 0, 1, 2
+STATS_COLS = 4  # {m, d, X_y, loss}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblmhead.so")
+_lib = None
+
+_i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+
+# (name, argtypes) of every entry point in include/lmhead.h
+_SIGNATURES = {
+    "lmhead_status_str": ([_i32], ctypes.c_char_p),
+    "lmhead_version": ([], _i32),
+    "lmhead_logits": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
+    "lmhead_xent_fwd": ([_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp], _i32),
+    "lmhead_xent_mean": ([_vp, _vp, _i32, _i64, _vp, _vp, _vp], _i32),
+    "lmhead_xent_bwd": ([_vp, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _i64, _i32, _i64, _i64,
+                         _vp], _i32),
+    "lmhead_dgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
+    "lmhead_wgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
+}
+
+
+class LmheadError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = int(status)
+        super().__init__(f"{fn}: {lmhead_status_str(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded ``liblmhead.so`` (ctypes) with every signature declared.
+    Raises if the library has not been built -- there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            "g.build()'` (hipcc, gfx950)")
+    handle = ctypes.CDLL(_LIB_PATH)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = handle
+    return handle
+
+
+def lmhead_status_str(status) -> str:
+    return lib().lmhead_status_str(int(status)).decode()
+
+
+def lmhead_version() -> int:
+    return int(lib().lmhead_version())
+
+
+# ------------------------------------------------------------- marshalling
+
+_DT = {"bf16": LMH_BF16, "fp32": LMH_FP32, "fp16": LMH_FP16,
+       torch.bfloat16: LMH_BF16, torch.float32: LMH_FP32, torch.float16: LMH_FP16}
+_TORCH_DT = {LMH_BF16: torch.bfloat16, LMH_FP32: torch.float32, LMH_FP16: torch.float16}
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    if dt not in _DT:
+        raise ValueError(f"unknown dtype {dt!r}")
+    return _DT[dt]
+
+
+def _check(fn, status):
+    if status != 0:
+        raise LmheadError(fn, status)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _mat(t, name, dtype):
+    """(pointer, ld) of a 2-D GPU tensor with a contiguous last dimension."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+    return _vp(t.data_ptr()), int(ld)
+
+
+def _vec(t, name, dtype, n):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() != n or (n > 1 and not t.is_contiguous()):
+        raise ValueError(f"{name}: expected {n} contiguous elements")
+    return _vp(t.data_ptr())
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# --------------------------------------------------------------- the calls
+
+def lmhead_logits(x, W, out=None, out_dtype="fp32", stream=None):
+    """logits[M, V] = x[M, K] . W[V, K]^T; out_dtype 'fp32' keeps the FP32
+    accumulator, 'bf16' rounds it (legacy); 'fp16' is rejected."""
+    code = _dtype_code(out_dtype)
+    px, ldx = _mat(x, "x", torch.bfloat16)
+    pw, ldw = _mat(W, "W", torch.bfloat16)
+    M, K = x.shape
+    V = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("x and W disagree on K")
+    if out is None:
+        if code not in (LMH_BF16, LMH_FP32):
+            _check("lmhead_logits", 1)
+        out = _empty((M, V), _TORCH_DT[code], x)
+    po, ldo = _mat(out, "out", out.dtype)
+    if out.shape != (M, V):
+        raise ValueError("out must be [M, V]")
+    _check("lmhead_logits", lib().lmhead_logits(px, ldx, pw, ldw, po, ldo, code, M, K, V,
+                                                _stream(stream)))
+    return out
+
+
+def lmhead_xent_fwd(logits, target, ignore_index=-100, loss=None, stats=None, stream=None):
+    """Fused CE forward: returns (loss [n], stats [n, 4] = {m, d, X_y, loss})."""
+    pz, ld = _mat(logits, "logits", torch.float32)
+    n, V = logits.shape
+    pt = _vec(target, "target", torch.int32, n)
+    if stats is None:
+        stats = _empty((n, STATS_COLS), torch.float32, logits)
+    if loss is None:
+        loss = _empty((n,), torch.float32, logits)
+    ps = _vec(stats, "stats", torch.float32, n * STATS_COLS)
+    pl = _vec(loss, "loss", torch.float32, n) if loss is not False else None
+    _check("lmhead_xent_fwd", lib().lmhead_xent_fwd(pz, ld, n, V, pt, int(ignore_index), pl, ps,
+                                                    _stream(stream)))
+    return (loss if loss is not False else None), stats
+
+
+def lmhead_xent_mean(loss, target, ignore_index=-100, mean=None, inv_nvalid=None, stream=None):
+    """Mean over non-ignored rows: returns (mean [1], inv_nvalid [1]) on the GPU."""
+    n = loss.numel()
+    pl = _vec(loss, "loss", torch.float32, n)
+    pt = _vec(target, "target", torch.int32, n)
+    if mean is None:
+        mean = _empty((1,), torch.float32, loss)
+    if inv_nvalid is None:
+        inv_nvalid = _empty((1,), torch.float32, loss)
+    pm = _vec(mean, "mean", torch.float32, 1)
+    pi = _vec(inv_nvalid, "inv_nvalid", torch.float32, 1)
+    _check("lmhead_xent_mean", lib().lmhead_xent_mean(pl, pt, int(ignore_index), n, pm, pi,
+                                                      _stream(stream)))
+    return mean, inv_nvalid
+
+
+def lmhead_xent_bwd(logits, stats, target, dloss, ignore_index=-100, dlogits=None,
+                    grad_dtype="fp32", in_place=False, stream=None):
+    """Fused CE backward: dlogits = dloss_i * (softmax - one_hot) in FP32.
+
+    dloss: a GPU fp32 tensor of 1 element (every row) or n elements (per row).
+    grad_dtype 'fp32' or 'bf16'; in_place=True writes over `logits` (fp32)."""
+    code = _dtype_code(grad_dtype)
+    pz, ld = _mat(logits, "logits", torch.float32)
+    n, V = logits.shape
+    ps = _vec(stats, "stats", torch.float32, n * STATS_COLS)
+    pt = _vec(target, "target", torch.int32, n)
+    if not isinstance(dloss, torch.Tensor) or not dloss.is_cuda or dloss.dtype != torch.float32:
+        raise TypeError("dloss: expected a GPU fp32 tensor")
+    if dloss.numel() == 1:
+        stride = 0
+    elif dloss.numel() == n and dloss.is_contiguous():
+        stride = 1
+    else:
+        raise ValueError("dloss must hold 1 or n_rows contiguous values")
+    pd = _vp(dloss.data_ptr())
+    if in_place:
+        dlogits = logits
+    elif dlogits is None:
+        if code not in (LMH_BF16, LMH_FP32):
+            _check("lmhead_xent_bwd", 1)
+        dlogits = _empty((n, V), _TORCH_DT[code], logits)
+    pg, ldg = _mat(dlogits, "dlogits", dlogits.dtype)
+    if dlogits.shape != (n, V):
+        raise ValueError("dlogits must be [n, V]")
+    _check("lmhead_xent_bwd", lib().lmhead_xent_bwd(pz, ld, ps, pt, int(ignore_index), pd, stride,
+                                                    pg, ldg, code, n, V, _stream(stream)))
+    return dlogits
+
+
+def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", stream=None):
+    """dX[M, K] = dlogits[M, V] . W[V, K] (bf16 operands, fp32 accumulation)."""
+    code = _dtype_code(dx_dtype)
+    pd, ldd = _mat(dlogits, "dlogits", torch.bfloat16)
+    pw, ldw = _mat(W, "W", torch.bfloat16)
+    M, V = dlogits.shape
+    K = W.shape[1]
+    if W.shape[0] != V:
+        raise ValueError("dlogits and W disagree on V")
+    if dX is None:
+        if code not in (LMH_BF16, LMH_FP32):
+            _check("lmhead_dgrad", 1)
+        dX = _empty((M, K), _TORCH_DT[code], dlogits)
+    px, ldx = _mat(dX, "dX", dX.dtype)
+    if dX.shape != (M, K):
+        raise ValueError("dX must be [M, K]")
+    _check("lmhead_dgrad", lib().lmhead_dgrad(pd, ldd, pw, ldw, px, ldx, code, M, K, V,
+                                              _stream(stream)))
+    return dX
+
+
+def lmhead_wgrad(dlogits, x, dW=None, accumulate=False, stream=None):
+    """dW[V, K] (+)= dlogits[M, V]^T . x[M, K] (bf16 operands, fp32 out)."""
+    pd, ldd = _mat(dlogits, "dlogits", torch.bfloat16)
+    px, ldx = _mat(x, "x", torch.bfloat16)
+    M, V = dlogits.shape
+    K = x.shape[1]
+    if x.shape[0] != M:
+        raise ValueError("dlogits and x disagree on M")
+    if dW is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing dW")
+        dW = _empty((V, K), torch.float32, dlogits)
+    pw, ldw = _mat(dW, "dW", torch.float32)
+    if dW.shape != (V, K):
+        raise ValueError("dW must be [V, K]")
+    _check("lmhead_wgrad", lib().lmhead_wgrad(pd, ldd, px, ldx, pw, ldw, int(bool(accumulate)),
+                                              M, K, V, _stream(stream)))
+    return dW

@@ -1,0 +1,285 @@
+// api.hip -- the C ABI of liblmhead.so (declared in include/lmhead.h).
+//
+// Every entry point validates its arguments on the host before any HIP call
+// and returns an LMH_ERR_* code without touching the GPU when they are
+// invalid; otherwise it enqueues its kernels on the caller's stream.
+#include "lmhead.h"
+
+#include "common.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxDim = static_cast<int64_t>(INT_MAX);
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+bool aligned4(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
+}
+
+// Byte range [lo, hi) touched by a row-major [rows x cols] matrix.
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t esz)
+{
+    Span s;
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = (rows <= 0 || cols <= 0)
+               ? s.lo
+               : s.lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * esz);
+    return s;
+}
+
+bool overlaps(const Span &a, const Span &b)
+{
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+int32_t launch_status(hipError_t e)
+{
+    return e == hipSuccess ? LMH_OK : LMH_ERR_LAUNCH;
+}
+
+// Common checks of a row-major matrix operand.
+int32_t check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld, int ld_multiple)
+{
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (rows == 0 || cols == 0)
+        return LMH_OK;
+    if (!p)
+        return LMH_ERR_NULL;
+    if (ld < cols)
+        return LMH_ERR_SHAPE;
+    if (!aligned16(p) || (ld % ld_multiple) != 0)
+        return LMH_ERR_ALIGN;
+    return LMH_OK;
+}
+
+#define LMH_TRY(expr)                 \
+    do {                              \
+        const int32_t _st = (expr);   \
+        if (_st != LMH_OK)            \
+            return _st;               \
+    } while (0)
+
+int32_t check_dtype_out(int32_t dt)
+{
+    return (dt == LMH_BF16 || dt == LMH_FP32) ? LMH_OK : LMH_ERR_DTYPE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lmhead_status_str(int32_t status)
+{
+    switch (status) {
+    case LMH_OK: return "LMH_OK";
+    case LMH_ERR_DTYPE: return "LMH_ERR_DTYPE: unsupported element type (bf16 or fp32 only)";
+    case LMH_ERR_SHAPE: return "LMH_ERR_SHAPE: bad size, leading dimension or stride";
+    case LMH_ERR_NULL: return "LMH_ERR_NULL: required pointer is NULL";
+    case LMH_ERR_ALIGN: return "LMH_ERR_ALIGN: pointer or leading dimension misaligned";
+    case LMH_ERR_ALIAS: return "LMH_ERR_ALIAS: output overlaps an input";
+    case LMH_ERR_LAUNCH: return "LMH_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown lmhead status";
+    }
+}
+
+int32_t lmhead_version(void)
+{
+    return 100;
+}
+
+int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, void *out,
+                      int64_t ldo, int32_t out_dtype, int64_t M, int64_t K, int64_t V,
+                      void *stream)
+{
+    LMH_TRY(check_dtype_out(out_dtype));
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim)
+        return LMH_ERR_SHAPE;
+    const int64_t osz = out_dtype == LMH_FP32 ? 4 : 2;
+    LMH_TRY(check_matrix(out, M, V, ldo, out_dtype == LMH_FP32 ? 4 : 8));
+    if (M == 0 || V == 0)
+        return LMH_OK;
+    if (K > 0) {
+        LMH_TRY(check_matrix(x, M, K, ldx, 8));
+        LMH_TRY(check_matrix(W, V, K, ldw, 8));
+        const Span so = span_of(out, M, V, ldo, osz);
+        if (overlaps(so, span_of(x, M, K, ldx, 2)) || overlaps(so, span_of(W, V, K, ldw, 2)))
+            return LMH_ERR_ALIAS;
+    }
+    lmh::GemmProblem p;
+    p.A = static_cast<const uint16_t *>(W);
+    p.lda = ldw;
+    p.B = static_cast<const uint16_t *>(x);
+    p.ldb = ldx;
+    p.D = out;
+    p.ldd = ldo;
+    p.R = V;
+    p.C = M;
+    p.P = K;
+    return launch_status(lmh::launch_gemm_logits(
+        p, out_dtype == LMH_FP32 ? lmh::Epi::kStoreF32 : lmh::Epi::kStoreBF16,
+        static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                        const int32_t *target, int32_t ignore_index, float *loss, float *stats,
+                        void *stream)
+{
+    if (n_rows < 0 || n_cols < 0 || n_rows > kMaxDim || n_cols > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (n_rows == 0)
+        return LMH_OK;
+    if (n_cols < 1)
+        return LMH_ERR_SHAPE;
+    LMH_TRY(check_matrix(logits, n_rows, n_cols, ld, 4));
+    if (!target || !stats)
+        return LMH_ERR_NULL;
+    if (!aligned16(stats) || !aligned4(target) || (loss && !aligned4(loss)))
+        return LMH_ERR_ALIGN;
+    const Span sz = span_of(logits, n_rows, n_cols, ld, 4);
+    const Span ss = span_of(stats, n_rows, 4, 4, 4);
+    if (overlaps(sz, ss) || overlaps(ss, span_of(target, 1, n_rows, n_rows, 4)))
+        return LMH_ERR_ALIAS;
+    if (loss) {
+        const Span sl = span_of(loss, 1, n_rows, n_rows, 4);
+        if (overlaps(sl, sz) || overlaps(sl, ss) || overlaps(sl, span_of(target, 1, n_rows, n_rows, 4)))
+            return LMH_ERR_ALIAS;
+    }
+    return launch_status(lmh::launch_xent_fwd(logits, ld, n_rows, n_cols, target, ignore_index,
+                                              loss, stats, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_xent_mean(const float *loss, const int32_t *target, int32_t ignore_index,
+                         int64_t n_rows, float *mean_out, float *inv_nvalid_out, void *stream)
+{
+    if (n_rows < 0 || n_rows > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (!mean_out && !inv_nvalid_out)
+        return LMH_OK;
+    if (n_rows > 0 && (!loss || !target))
+        return LMH_ERR_NULL;
+    if ((loss && !aligned4(loss)) || (target && !aligned4(target)) ||
+        (mean_out && !aligned4(mean_out)) || (inv_nvalid_out && !aligned4(inv_nvalid_out)))
+        return LMH_ERR_ALIGN;
+    return launch_status(lmh::launch_xent_mean(loss, target, ignore_index, n_rows, mean_out,
+                                               inv_nvalid_out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_xent_bwd(const float *logits, int64_t ld, const float *stats,
+                        const int32_t *target, int32_t ignore_index, const float *dloss,
+                        int64_t dloss_stride, void *dlogits, int64_t ldg, int32_t grad_dtype,
+                        int64_t n_rows, int64_t n_cols, void *stream)
+{
+    LMH_TRY(check_dtype_out(grad_dtype));
+    if (n_rows < 0 || n_cols < 0 || n_rows > kMaxDim || n_cols > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (dloss_stride != 0 && dloss_stride != 1)
+        return LMH_ERR_SHAPE;
+    if (n_rows == 0)
+        return LMH_OK;
+    if (n_cols < 1)
+        return LMH_ERR_SHAPE;
+    const bool bf16 = grad_dtype == LMH_BF16;
+    LMH_TRY(check_matrix(logits, n_rows, n_cols, ld, 4));
+    LMH_TRY(check_matrix(dlogits, n_rows, n_cols, ldg, bf16 ? 8 : 4));
+    if (!stats || !target || !dloss)
+        return LMH_ERR_NULL;
+    if (!aligned16(stats) || !aligned4(target) || !aligned4(dloss))
+        return LMH_ERR_ALIGN;
+    const Span sz = span_of(logits, n_rows, n_cols, ld, 4);
+    const Span sg = span_of(dlogits, n_rows, n_cols, ldg, bf16 ? 2 : 4);
+    const bool in_place = static_cast<const void *>(dlogits) == static_cast<const void *>(logits);
+    if (in_place) {
+        if (bf16 || ldg != ld)
+            return LMH_ERR_ALIAS;
+    } else if (overlaps(sz, sg)) {
+        return LMH_ERR_ALIAS;
+    }
+    const int64_t ndl = dloss_stride == 0 ? 1 : n_rows;
+    if (overlaps(sg, span_of(stats, n_rows, 4, 4, 4)) ||
+        overlaps(sg, span_of(target, 1, n_rows, n_rows, 4)) ||
+        overlaps(sg, span_of(dloss, 1, ndl, ndl, 4)))
+        return LMH_ERR_ALIAS;
+    return launch_status(lmh::launch_xent_bwd(logits, ld, stats, target, ignore_index, dloss,
+                                              dloss_stride, dlogits, ldg, bf16, n_rows, n_cols,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ldw, void *dX,
+                     int64_t ldx, int32_t dx_dtype, int64_t M, int64_t K, int64_t V, void *stream)
+{
+    LMH_TRY(check_dtype_out(dx_dtype));
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim)
+        return LMH_ERR_SHAPE;
+    const int64_t osz = dx_dtype == LMH_FP32 ? 4 : 2;
+    LMH_TRY(check_matrix(dX, M, K, ldx, dx_dtype == LMH_FP32 ? 4 : 8));
+    if (M == 0 || K == 0)
+        return LMH_OK;
+    if (V > 0) {
+        LMH_TRY(check_matrix(dlogits, M, V, ldd, 8));
+        LMH_TRY(check_matrix(W, V, K, ldw, 8));
+        const Span so = span_of(dX, M, K, ldx, osz);
+        if (overlaps(so, span_of(dlogits, M, V, ldd, 2)) || overlaps(so, span_of(W, V, K, ldw, 2)))
+            return LMH_ERR_ALIAS;
+    }
+    lmh::GemmProblem p;
+    p.A = static_cast<const uint16_t *>(W);  // stored [V][K] = [P][R]
+    p.lda = ldw;
+    p.B = static_cast<const uint16_t *>(dlogits);  // [M][V] = [C][P]
+    p.ldb = ldd;
+    p.D = dX;
+    p.ldd = ldx;
+    p.R = K;
+    p.C = M;
+    p.P = V;
+    return launch_status(lmh::launch_gemm_dgrad(
+        p, dx_dtype == LMH_FP32 ? lmh::Epi::kStoreF32 : lmh::Epi::kStoreBF16,
+        static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ldx, float *dW,
+                     int64_t ldw, int32_t accumulate, int64_t M, int64_t K, int64_t V,
+                     void *stream)
+{
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim)
+        return LMH_ERR_SHAPE;
+    LMH_TRY(check_matrix(dW, V, K, ldw, 4));
+    if (V == 0 || K == 0)
+        return LMH_OK;
+    if (M == 0 && accumulate)
+        return LMH_OK;
+    if (M > 0) {
+        LMH_TRY(check_matrix(dlogits, M, V, ldd, 8));
+        LMH_TRY(check_matrix(x, M, K, ldx, 8));
+        const Span so = span_of(dW, V, K, ldw, 4);
+        if (overlaps(so, span_of(dlogits, M, V, ldd, 2)) || overlaps(so, span_of(x, M, K, ldx, 2)))
+            return LMH_ERR_ALIAS;
+    }
+    lmh::GemmProblem p;
+    p.A = static_cast<const uint16_t *>(x);  // stored [M][K] = [P][R]
+    p.lda = ldx;
+    p.B = static_cast<const uint16_t *>(dlogits);  // stored [M][V] = [P][C]
+    p.ldb = ldd;
+    p.D = dW;
+    p.ldd = ldw;
+    p.R = K;
+    p.C = V;
+    p.P = M;
+    return launch_status(lmh::launch_gemm_wgrad(
+        p, accumulate ? lmh::Epi::kAccumF32 : lmh::Epi::kStoreF32,
+        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+"""Host-side tests of the C-ABI boundary (no GPU needed).
+
+Every invalid-argument path of include/lmhead.h is validated on the host
+before any HIP call, so these calls return their LMH_ERR_* code without a
+GPU.  Pointers below are fake addresses: no call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lm_head_fp32_amd as lmh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead.h")
+
+OK, DTYPE, SHAPE, NULL, ALIGN, ALIAS = 0, 1, 2, 3, 4, 5
+BF16, FP32, FP16 = lmh.LMH_BF16, lmh.LMH_FP32, lmh.LMH_FP16
+
+A = 0x10000000      # fake, 16-byte aligned device addresses far apart
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lmh.library_path()):
+        pytest.skip("liblmhead.so not built")
+    return lmh.lib()
+
+
+def _declared_symbols():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(lmhead_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_symbols() == sorted(lmh._SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_symbols():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(L):
+    assert lmh.lmhead_version() == 100
+    assert lmh.lmhead_status_str(0) == "LMH_OK"
+    for s in range(1, 7):
+        assert lmh.lmhead_status_str(s).startswith("LMH_ERR_")
+    assert "unknown" in lmh.lmhead_status_str(99)
+
+
+def test_logits_validation(L):
+    f = L.lmhead_logits
+    # fp16 output is rejected, as is an unknown dtype (the pages' option accepts
+    # bf16 and fp32 only)
+    assert f(A, 64, B, 64, C, 128, FP16, 16, 64, 128, None) == DTYPE
+    assert f(A, 64, B, 64, C, 128, 7, 16, 64, 128, None) == DTYPE
+    assert f(A, 64, B, 64, C, 128, FP32, -1, 64, 128, None) == SHAPE
+    assert f(A, 64, B, 64, C, 120, FP32, 16, 64, 128, None) == SHAPE   # ldo < V
+    assert f(A, 56, B, 64, C, 128, FP32, 16, 64, 128, None) == SHAPE   # ldx < K
+    assert f(None, 64, B, 64, C, 128, FP32, 16, 64, 128, None) == NULL
+    assert f(A, 64, None, 64, C, 128, FP32, 16, 64, 128, None) == NULL
+    assert f(A, 64, B, 64, None, 128, FP32, 16, 64, 128, None) == NULL
+    assert f(A + 2, 64, B, 64, C, 128, FP32, 16, 64, 128, None) == ALIGN
+    assert f(A, 68, B, 64, C, 128, FP32, 16, 64, 128, None) == ALIGN    # bf16 ld % 8
+    assert f(A, 64, B, 64, C, 130, FP32, 16, 64, 130, None) == ALIGN    # fp32 ld % 4
+    assert f(A, 64, B, 64, C, 132, BF16, 16, 64, 132, None) == ALIGN    # bf16 out ld % 8
+    assert f(A, 64, B, 64, A + 64, 128, FP32, 16, 64, 128, None) == ALIAS
+    assert f(A, 64, B, 64, B, 128, FP32, 16, 64, 128, None) == ALIAS
+    # empty outputs are no-ops that touch nothing
+    assert f(None, 64, None, 64, None, 128, FP32, 0, 64, 128, None) == OK
+    assert f(None, 64, None, 64, None, 128, FP32, 16, 64, 0, None) == OK
+
+
+def test_xent_fwd_validation(L):
+    f = L.lmhead_xent_fwd
+    assert f(A, 1024, -1, 1024, B, -100, C, D, None) == SHAPE
+    assert f(A, 1024, 8, 0, B, -100, C, D, None) == SHAPE
+    assert f(A, 1000, 8, 1024, B, -100, C, D, None) == SHAPE          # ld < n_cols
+    assert f(A, 1026, 8, 1024, B, -100, C, D, None) == ALIGN          # ld % 4
+    assert f(A + 4, 1024, 8, 1024, B, -100, C, D, None) == ALIGN
+    assert f(A, 1024, 8, 1024, B, -100, C, D + 4, None) == ALIGN      # stats 16-B
+    assert f(A, 1024, 8, 1024, B + 2, -100, C, D, None) == ALIGN      # target 4-B
+    assert f(None, 1024, 8, 1024, B, -100, C, D, None) == NULL
+    assert f(A, 1024, 8, 1024, None, -100, C, D, None) == NULL
+    assert f(A, 1024, 8, 1024, B, -100, C, None, None) == NULL
+    assert f(A, 1024, 8, 1024, B, -100, C, A + 256, None) == ALIAS    # stats over logits
+    assert f(A, 1024, 8, 1024, B, -100, A, D, None) == ALIAS          # loss over logits
+    assert f(A, 1024, 8, 1024, B, -100, D + 16, D, None) == ALIAS     # loss over stats
+    assert f(None, 1024, 0, 1024, None, -100, None, None, None) == OK
+
+
+def test_xent_bwd_validation(L):
+    f = L.lmhead_xent_bwd
+    args = dict(logits=A, ld=1024, stats=B, target=C, ign=-100, dloss=D, ds=0,
+                g=E, ldg=1024, dt=FP32, n=8, V=1024)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["logits"], a["ld"], a["stats"], a["target"], a["ign"], a["dloss"], a["ds"],
+                 a["g"], a["ldg"], a["dt"], a["n"], a["V"], None)
+
+    assert call(dt=FP16) == DTYPE
+    assert call(ds=2) == SHAPE
+    assert call(ds=-1) == SHAPE
+    assert call(n=-1) == SHAPE
+    assert call(V=0) == SHAPE
+    assert call(stats=None) == NULL
+    assert call(dloss=None) == NULL
+    assert call(g=None) == NULL
+    assert call(stats=B + 8) == ALIGN
+    assert call(ldg=1028, dt=BF16) == ALIGN
+    assert call(g=A, ldg=1024, dt=BF16) == ALIAS        # bf16 in place is rejected
+    assert call(g=A, ldg=2048, ld=1024) == ALIAS        # in place needs the same ld
+    assert call(g=A + 64) == ALIAS                      # partial overlap
+    assert call(g=B - 64) == ALIAS                      # gradient over the stats
+    assert call(n=0) == OK
+
+
+def test_mean_validation(L):
+    f = L.lmhead_xent_mean
+    assert f(A, B, -100, -1, C, D, None) == SHAPE
+    assert f(None, B, -100, 8, C, D, None) == NULL
+    assert f(A + 2, B, -100, 8, C, D, None) == ALIGN
+    assert f(A, B, -100, 8, None, None, None) == OK       # nothing requested
+
+
+def test_dgrad_wgrad_validation(L):
+    g = L.lmhead_dgrad
+    assert g(A, 128, B, 64, C, 64, FP16, 16, 64, 128, None) == DTYPE
+    assert g(A, 120, B, 64, C, 64, BF16, 16, 64, 128, None) == SHAPE   # ldd < V
+    assert g(A, 128, B, 64, C, 60, FP32, 16, 64, 128, None) == SHAPE   # ldx < K
+    assert g(A, 128, B, 64, A, 64, BF16, 16, 64, 128, None) == ALIAS
+    assert g(A + 8, 128, B, 64, C, 64, BF16, 16, 64, 128, None) == ALIGN
+    assert g(None, 128, B, 64, C, 64, BF16, 16, 64, 128, None) == NULL
+    w = L.lmhead_wgrad
+    assert w(A, 128, B, 64, C, 60, 0, 16, 64, 128, None) == SHAPE       # ldw < K
+    assert w(A, 128, B, 64, C, 66, 0, 16, 64, 128, None) == ALIGN       # fp32 ld % 4
+    assert w(A, 128, B, 64, B, 64, 0, 16, 64, 128, None) == ALIAS
+    assert w(None, 128, B, 64, C, 64, 0, 16, 64, 128, None) == NULL
+    assert w(None, 128, None, 64, C, 64, 1, 0, 64, 128, None) == OK     # M = 0, accumulate
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        lmh.lmhead_logits(x, x)

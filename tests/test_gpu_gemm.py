@@ -1,0 +1,207 @@
+"""GPU parity of the three GEMMs (logits, dgrad, wgrad) against the FP64
+oracle, through the C ABI (via the thin binding).
+
+Bar: bit-exact on integer operands (every FP32 partial sum is exact when
+K * 8^2 < 2^24, Megatron-LM "Add mixed-precision (FP32) LM output logits",
+section "Tests"); on random operands |gpu - L| <= 1e-5 * sum_k |x_k w_k|.
+BF16 outputs are bit-exact on integers (round-to-nearest-even of the exact
+value) and within 1e-5 * S plus half a BF16 spacing on random operands."""
+import numpy as np
+import pytest
+import torch
+
+import lm_head_fp32_amd as lmh
+import oracle
+import workloads
+from gpu_util import (assert_gemm_close, dev_bf16, host_bits, host_f32, padded_out,
+                      padding_untouched)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lmh.lib()  # fail loudly if the library is missing
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _f32_bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+# ----------------------------------------------------------------- logits
+
+def test_logits_tiny_exact_fp32_and_bf16():
+    """x [16 x 512], W [1024 x 512] integers in [-8, 8], seed 1234: FP32
+    logits bit-exact; BF16 logits bit-exact to RNE of the exact value."""
+    inp = workloads.tiny_exact()
+    _say("tiny_exact logits")
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    out = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    outb = lmh.lmhead_logits(x, W, out_dtype="bf16")
+    torch.cuda.synchronize()
+    L, _ = oracle.logits(inp.x, inp.W)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(L.astype(np.float32)))
+    assert np.array_equal(host_bits(outb), oracle.round_bf16(L))
+    # the legacy BF16 output really loses bits on this workload
+    assert np.any(oracle.bf16_bits_to_f64(host_bits(outb)) != L)
+
+
+@pytest.mark.parametrize("K", workloads.INT_SWEEP_K)
+def test_logits_integer_sweep_v32768(K):
+    """The pages' integer sweep: 16 x K activations, 32,768 x K weights,
+    K = 512 ... 16384; FP32 logits bit-exact (rows sampled for the oracle)."""
+    inp = workloads.integer_gemm(16, K, 32768, seed=workloads.SEED, with_targets=False)
+    _say(f"int sweep K={K}")
+    out = lmh.lmhead_logits(dev_bf16(inp.x), dev_bf16(inp.W), out_dtype="fp32")
+    torch.cuda.synchronize()
+    rows = np.array([0, 7, 15])
+    L, _ = oracle.logits(inp.x, inp.W, rows=rows)
+    assert np.array_equal(_f32_bits(host_f32(out)[rows]), _f32_bits(L.astype(np.float32)))
+
+
+def _up(v, m):
+    return (v + m - 1) // m * m
+
+
+@pytest.mark.parametrize("M,K,V,pad", [
+    (1, 8, 1, 0), (3, 24, 5, 8), (17, 72, 65, 0), (33, 200, 130, 16), (130, 64, 257, 8),
+    (64, 136, 300, 0), (257, 96, 129, 24), (31, 1000, 511, 0), (40, 8, 1000, 0),
+    (7, 13, 9, 0), (19, 77, 33, 8),
+])
+def test_logits_ragged_integer_exact(M, K, V, pad):
+    """Ragged M, K, V (partial tiles on every edge, K not a multiple of the
+    64-wide stage nor of 8), padded leading dimensions; padding never written."""
+    inp = workloads.integer_gemm(M, K, V, seed=M * 1000 + K + V, with_targets=False)
+    _say(f"ragged logits M={M} K={K} V={V} pad={pad}")
+    x = dev_bf16(inp.x, _up(K, 8) + pad)
+    W = dev_bf16(inp.W, _up(K, 8) + 2 * pad)
+    out = padded_out(M, V, _up(V, 4) + pad, torch.float32)
+    outb = padded_out(M, V, _up(V, 8) + pad, torch.bfloat16)
+    lmh.lmhead_logits(x, W, out=out, out_dtype="fp32")
+    lmh.lmhead_logits(x, W, out=outb, out_dtype="bf16")
+    torch.cuda.synchronize()
+    L, _ = oracle.logits(inp.x, inp.W)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(L.astype(np.float32)))
+    assert np.array_equal(host_bits(outb), oracle.round_bf16(L))
+    assert padding_untouched(out) and padding_untouched(outb)
+
+
+def test_logits_k_zero_writes_zeros():
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((12, 0), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((5, 12), float("nan"), device="cuda")
+    lmh.lmhead_logits(x, W, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item()
+
+
+def test_logits_fp16_rejected():
+    x = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lmh.LmheadError) as e:
+        lmh.lmhead_logits(x, x, out=torch.zeros((4, 4), dtype=torch.float16, device="cuda"),
+                          out_dtype="fp16")
+    assert e.value.status == 1
+
+
+def test_logits_lmhead_128_random_full():
+    """M=128, K=4096, V=32768, x ~ N(0,1), W ~ N(0, 0.02^2): every logit
+    within 1e-5 * S of the FP64 sum; BF16 output within S-bound + half ulp."""
+    inp = workloads.lmhead_128()
+    _say("lmhead_128 random logits")
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    out = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    outb = lmh.lmhead_logits(x, W, out_dtype="bf16")
+    torch.cuda.synchronize()
+    L, S = oracle.logits(inp.x, inp.W)
+    assert_gemm_close(host_f32(out), L, S, 1e-5, "fp32 logits")
+    gb = oracle.bf16_bits_to_f64(host_bits(outb))
+    half_ulp = np.abs(L) * 2.0 ** -8
+    assert np.all(np.abs(gb - L) <= 1e-5 * S + half_ulp + 1e-30)
+
+
+def test_logits_lmhead_1024_random_sampled():
+    """M=1024, K=8192, V=32768 (the benchmark's launch shape): 24 sampled
+    rows x all V columns within 1e-5 * S; run twice, bitwise identical."""
+    inp = workloads.lmhead_1024()
+    _say("lmhead_1024 random logits")
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    out = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    out2 = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    rows = np.concatenate([np.arange(0, 1024, 64), [1, 255, 256, 511, 512, 767, 1022, 1023]])
+    L, S = oracle.logits(inp.x, inp.W, rows=rows)
+    assert_gemm_close(host_f32(out)[rows], L, S, 1e-5, "fp32 logits 1024")
+
+
+# ------------------------------------------------------------------ dgrad
+
+@pytest.mark.parametrize("M,K,V", [(16, 64, 128), (33, 72, 130), (130, 256, 1000), (64, 8, 64),
+                                   (5, 520, 4100), (9, 20, 37)])
+def test_dgrad_integer_exact(M, K, V):
+    """dX = dl . W on integers: bit-exact FP32 and BF16 outputs; ragged M, K,
+    V with padded leading dimensions."""
+    dl_bits, W_bits = workloads.integer_operands([(M, V), (V, K)], seed=7 + M + K + V)
+    _say(f"dgrad int M={M} K={K} V={V}")
+    dl, W = dev_bf16(dl_bits, _up(V, 8)), dev_bf16(W_bits, _up(K, 8))
+    dx = padded_out(M, K, _up(K, 4) + 4, torch.float32)
+    lmh.lmhead_dgrad(dl, W, dX=dx, dx_dtype="fp32")
+    dxb = padded_out(M, K, _up(K, 8) + 8, torch.bfloat16)
+    lmh.lmhead_dgrad(dl, W, dX=dxb, dx_dtype="bf16")
+    torch.cuda.synchronize()
+    ref, _ = oracle.dgrad(dl_bits, W_bits)
+    assert np.array_equal(_f32_bits(host_f32(dx)), _f32_bits(ref.astype(np.float32)))
+    assert np.array_equal(host_bits(dxb), oracle.round_bf16(ref))
+    assert padding_untouched(dx) and padding_untouched(dxb)
+
+
+def test_dgrad_random_sampled():
+    """dX = dl . W at M=1024, K=8192, V=32768 with synthetic BF16 dl."""
+    rng = np.random.default_rng(workloads.SEED + 3)
+    dl_bits = workloads.normal_bf16(rng, (1024, 32768), 1e-3)
+    W_bits = workloads.normal_bf16(rng, (32768, 8192), 0.02)
+    _say("dgrad random 1024x8192x32768")
+    dx = lmh.lmhead_dgrad(dev_bf16(dl_bits), dev_bf16(W_bits), dx_dtype="fp32")
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 100, 511, 512, 1000, 1023])
+    ref, S = oracle.dgrad(dl_bits, W_bits, rows=rows)
+    assert_gemm_close(host_f32(dx)[rows], ref, S, 1e-5, "dgrad")
+
+
+# ------------------------------------------------------------------ wgrad
+
+@pytest.mark.parametrize("M,K,V", [(16, 64, 128), (33, 72, 136), (130, 256, 1000), (8, 8, 8),
+                                   (300, 40, 520), (21, 20, 130)])
+def test_wgrad_integer_exact_and_accumulate(M, K, V):
+    """dW = dl^T . x on integers: bit-exact, then accumulate doubles it."""
+    dl_bits, x_bits = workloads.integer_operands([(M, V), (M, K)], seed=11 + M + K + V)
+    _say(f"wgrad int M={M} K={K} V={V}")
+    dl, x = dev_bf16(dl_bits, _up(V, 8)), dev_bf16(x_bits, _up(K, 8))
+    dw = padded_out(V, K, _up(K, 4) + 4, torch.float32)
+    lmh.lmhead_wgrad(dl, x, dW=dw)
+    torch.cuda.synchronize()
+    ref, _ = oracle.wgrad(dl_bits, x_bits)
+    assert np.array_equal(_f32_bits(host_f32(dw)), _f32_bits(ref.astype(np.float32)))
+    assert padding_untouched(dw)
+    lmh.lmhead_wgrad(dl, x, dW=dw, accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_f32_bits(host_f32(dw)), _f32_bits((2 * ref).astype(np.float32)))
+
+
+def test_wgrad_random_sampled():
+    """dW = dl^T . x at M=1024, K=8192, V=32768 with synthetic BF16 dl."""
+    rng = np.random.default_rng(workloads.SEED + 4)
+    dl_bits = workloads.normal_bf16(rng, (1024, 32768), 1e-3)
+    x_bits = workloads.normal_bf16(rng, (1024, 8192), 1.0)
+    _say("wgrad random 1024x8192x32768")
+    dw = lmh.lmhead_wgrad(dev_bf16(dl_bits), dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    rows = np.array([0, 5, 4095, 4096, 20000, 32767])
+    ref, S = oracle.wgrad(dl_bits, x_bits, rows=rows)
+    assert_gemm_close(host_f32(dw)[rows], ref, S, 1e-5, "wgrad")

@@ -1,0 +1,278 @@
+"""GPU parity of the fused cross-entropy (forward stats, mean, backward)
+against the FP64 oracle, through the C ABI (via the thin binding).
+
+Bars: m and X_y bit-exact (selections); d and loss within 1e-5 relative
+(loss with an absolute floor below |loss| = 1); FP32 dlogits within 1e-6
+absolute; BF16 dlogits bit-identical to round-to-nearest-even of the FP32
+dlogits of the same kernel; in-place bit-identical to out-of-place; two runs
+bit-identical.  The n_rows x 4 record and the FP32 backward follow
+Transformer Engine "[Pytorch] change fused cross entropy backward grad to
+fp32 and reduce one read/..." (discussion; sections "Description",
+"Changes")."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lm_head_fp32_amd as lmh
+import oracle
+import workloads
+from gpu_util import (assert_loss_close, dev_bf16, dev_f32, dev_i32, host_f32, padded_out,
+                      padding_untouched)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lmh.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _check_stats(st_gpu, st_ref, what=""):
+    """m, X bit-exact; d within 1e-5 rel; loss within 1e-5 rel (floor 1)."""
+    assert np.array_equal(_bits(st_gpu[:, 0]), _bits(st_ref[:, 0].astype(np.float32))), what + " m"
+    assert np.array_equal(_bits(st_gpu[:, 2]), _bits(st_ref[:, 2].astype(np.float32))), what + " X"
+    assert np.all(np.abs(st_gpu[:, 1] - st_ref[:, 1]) <= 1e-5 * st_ref[:, 1]), what + " d"
+    assert_loss_close(st_gpu[:, 3], st_ref[:, 3], 1e-5, what + " loss")
+
+
+def _check_grad(g_gpu, g_ref, tol=1e-6, what="dlogits"):
+    err = np.abs(g_gpu.astype(np.float64) - g_ref)
+    if not np.all(err <= tol):
+        i = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: max err {err[i]} at {i} gpu={g_gpu[i]} ref={g_ref[i]}")
+
+
+def _run_chain(z_dev, t_dev, ignore, grad_dtype="fp32"):
+    loss, st = lmh.lmhead_xent_fwd(z_dev, t_dev, ignore)
+    mean, inv = lmh.lmhead_xent_mean(loss, t_dev, ignore)
+    g = lmh.lmhead_xent_bwd(z_dev, st, t_dev, inv, ignore, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return loss, st, mean, inv, g
+
+
+# ------------------------------------------------------------ tiny exact
+
+def test_tiny_exact_chain():
+    """x [16 x 512] . W [1024 x 512]^T integers -> FP32 logits (bit-exact) ->
+    CE fwd -> mean (dloss = 1/16) -> FP32 bwd; the oracle runs its own chain."""
+    inp = workloads.tiny_exact()
+    _say("tiny_exact chain")
+    logits = lmh.lmhead_logits(dev_bf16(inp.x), dev_bf16(inp.W), out_dtype="fp32")
+    t = dev_i32(inp.target)
+    loss, st, mean, inv, g = _run_chain(logits, t, -100)
+    L, _ = oracle.logits(inp.x, inp.W)
+    z = L.astype(np.float32)                      # exact: integer logits < 2^24
+    assert np.array_equal(_bits(host_f32(logits)), _bits(z))
+    st_ref = oracle.xent_fwd(z, inp.target, -100)
+    _check_stats(host_f32(st), st_ref, "tiny")
+    assert np.array_equal(_bits(host_f32(loss)), _bits(host_f32(st)[:, 3]))
+    m_ref, inv_ref, nv = oracle.xent_mean(st_ref[:, 3], inp.target, -100)
+    assert nv == 16 and host_f32(inv)[0] == np.float32(1.0 / 16)
+    assert_loss_close(host_f32(mean), [m_ref], 1e-5, "mean")
+    g_ref = oracle.xent_bwd(z, inp.target, -100, inv_ref)
+    _check_grad(host_f32(g), g_ref)
+
+
+# ------------------------------------------------------------ closed forms
+
+@pytest.mark.parametrize("V", [1024, 32768, 131072])
+@pytest.mark.parametrize("c", [0.0, 7.25])
+def test_uniform_logits_closed_form(V, c):
+    """All logits equal: m = c, d = V exactly, loss = ln V; with dloss = 1/16
+    the gradient is exactly dloss/V off target and dloss/V - dloss on it."""
+    n = 4
+    _say(f"uniform V={V} c={c}")
+    z = torch.full((n, V), c, dtype=torch.float32, device="cuda")
+    tgt = np.array([0, V - 1, 3, V // 2], dtype=np.int32)
+    t = dev_i32(tgt)
+    loss, st = lmh.lmhead_xent_fwd(z, t)
+    dl = torch.full((1,), 1.0 / 16, device="cuda")
+    g = lmh.lmhead_xent_bwd(z, st, t, dl)
+    torch.cuda.synchronize()
+    s = host_f32(st)
+    assert np.all(s[:, 0] == np.float32(c)) and np.all(s[:, 2] == np.float32(c))
+    assert np.all(s[:, 1] == np.float32(V))
+    assert np.allclose(s[:, 3], math.log(V), rtol=1e-6, atol=0)
+    gh = host_f32(g)
+    for i, y in enumerate(tgt):
+        expect = np.full(V, np.float32(1.0 / 16 / V))
+        expect[y] = np.float32(1.0 / 16 / V - 1.0 / 16)
+        assert np.array_equal(_bits(gh[i]), _bits(expect))
+
+
+def test_vocab_one_and_two():
+    """V = 1: loss 0, gradient 0.  V = 2: loss = log1p(exp(z_o - z_y)) and
+    grad_y = -dloss * sigmoid(z_o - z_y) = -grad_o (closed forms)."""
+    z1 = dev_f32(np.array([[3.5], [-2.0], [0.0]], np.float32), ld=4)
+    t1 = dev_i32(np.array([0, 0, -100]))
+    loss, st = lmh.lmhead_xent_fwd(z1, t1)
+    g = lmh.lmhead_xent_bwd(z1, st, t1, torch.full((1,), 0.5, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.all(host_f32(loss) == 0) and np.all(host_f32(g) == 0)
+    zz = np.array([[1.25, -0.5], [4.0, 4.5], [-3.0, 9.0]], np.float32)
+    tt = np.array([0, 1, 0], np.int32)
+    z2 = dev_f32(zz, ld=4)
+    loss, st = lmh.lmhead_xent_fwd(z2, dev_i32(tt))
+    g = lmh.lmhead_xent_bwd(z2, st, dev_i32(tt), torch.full((1,), 0.25, device="cuda"))
+    torch.cuda.synchronize()
+    lh, gh = host_f32(loss), host_f32(g)
+    for i, y in enumerate(tt):
+        o = 1 - y
+        delta = float(zz[i, o]) - float(zz[i, y])
+        assert math.isclose(lh[i], math.log1p(math.exp(delta)), rel_tol=1e-5, abs_tol=1e-6)
+        sig = 1.0 / (1.0 + math.exp(-delta))
+        assert abs(gh[i, y] + 0.25 * sig) <= 1e-6 and abs(gh[i, o] - 0.25 * sig) <= 1e-6
+
+
+# ------------------------------------------------------------ edge shapes
+
+@pytest.mark.parametrize("n,V", [(1, 1), (3, 2), (5, 3), (17, 5), (4, 63), (9, 64), (33, 65),
+                                 (2, 1023), (600, 257), (700, 4097), (3, 40000)])
+@pytest.mark.parametrize("dloss_mode", ["scalar", "per_row"])
+def test_edge_shapes_random(n, V, dloss_mode):
+    """Ragged V (tails of 1-3 columns, one partial block), both launch
+    shapes (n < 512 and n >= 512), padded ld with untouched padding, ignored
+    rows, a custom ignore value, scalar and per-row dloss."""
+    rng = np.random.default_rng(n * 7919 + V)
+    inp = workloads.xent_logits(n, V, sigma=2.0, spike_frac=0.1, spike=30.0, ignore_frac=0.2,
+                                seed=n * 31 + V)
+    ignore = -100 if V % 2 else 7777
+    tgt = inp.target.copy()
+    tgt[tgt == -100] = ignore
+    _say(f"edge n={n} V={V} {dloss_mode} ignore={ignore}")
+    ld = (V + 3) // 4 * 4 + 4
+    z = dev_f32(inp.logits, ld)
+    t = dev_i32(tgt)
+    loss, st = lmh.lmhead_xent_fwd(z, t, ignore)
+    if dloss_mode == "scalar":
+        dl_host = np.float32(0.375)
+        dl = torch.full((1,), float(dl_host), device="cuda")
+        dl_ref = float(dl_host)
+    else:
+        dl_host = rng.uniform(-1, 1, n).astype(np.float32)
+        dl = torch.from_numpy(dl_host).cuda()
+        dl_ref = dl_host.astype(np.float64)
+    g = padded_out(n, V, ld + 4, torch.float32)
+    lmh.lmhead_xent_bwd(z, st, t, dl, ignore, dlogits=g)
+    gb = padded_out(n, V, (V + 7) // 8 * 8 + 8, torch.bfloat16)
+    lmh.lmhead_xent_bwd(z, st, t, dl, ignore, dlogits=gb, grad_dtype="bf16")
+    torch.cuda.synchronize()
+    st_ref = oracle.xent_fwd(inp.logits, tgt, ignore)
+    _check_stats(host_f32(st), st_ref, f"n={n} V={V}")
+    g_ref = oracle.xent_bwd(inp.logits, tgt, ignore, dl_ref)
+    _check_grad(host_f32(g), g_ref)
+    assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
+    assert padding_untouched(g) and padding_untouched(gb)
+    # gradient rows sum to zero
+    rs = np.abs(host_f32(g).astype(np.float64).sum(axis=1))
+    scale = np.abs(np.broadcast_to(dl_ref, (n,)))
+    assert np.all(rs <= 1e-5 * scale + 1e-7)
+
+
+def test_all_rows_ignored_and_bad_target():
+    V = 100
+    z = dev_f32(np.random.default_rng(1).normal(0, 1, (6, V)).astype(np.float32))
+    t = dev_i32(np.full(6, -100))
+    loss, st = lmh.lmhead_xent_fwd(z, t)
+    mean, inv = lmh.lmhead_xent_mean(loss, t)
+    g = lmh.lmhead_xent_bwd(z, st, t, inv)
+    torch.cuda.synchronize()
+    assert host_f32(mean)[0] == 0 and host_f32(inv)[0] == 0
+    assert np.all(host_f32(g) == 0) and np.all(host_f32(loss) == 0)
+    # a target outside [0, V) that is not ignore_index yields a NaN row only
+    tb = dev_i32(np.array([1, V, 2, -5, 3, 4]))
+    loss, st = lmh.lmhead_xent_fwd(z, tb)
+    g = lmh.lmhead_xent_bwd(z, st, tb, torch.full((1,), 1.0, device="cuda"))
+    torch.cuda.synchronize()
+    lh, gh = host_f32(loss), host_f32(g)
+    assert np.isnan(lh[[1, 3]]).all() and np.isfinite(lh[[0, 2, 4, 5]]).all()
+    assert np.isnan(gh[[1, 3]]).all() and np.isfinite(gh[[0, 2, 4, 5]]).all()
+
+
+def test_empty_rows_noop():
+    z = torch.empty((0, 16), device="cuda")
+    t = torch.empty((0,), dtype=torch.int32, device="cuda")
+    loss, st = lmh.lmhead_xent_fwd(z, t)
+    mean, inv = lmh.lmhead_xent_mean(loss, t)
+    torch.cuda.synchronize()
+    assert host_f32(mean)[0] == 0 and host_f32(inv)[0] == 0
+
+
+# ------------------------------------------------- benchmark-shaped rows
+
+def test_xent_1024x32768_bf16_grads_and_determinism():
+    """n=1024, V=32768 (the CE launch shape of the M=1024 step), BF16 grads:
+    stats and FP32 grads on sampled rows vs the oracle; BF16 == RNE(FP32);
+    two runs bit-identical."""
+    inp = workloads.xent_logits(1024, 32768, sigma=1.8, spike_frac=0.0, ignore_frac=0.0,
+                                seed=workloads.SEED + 5)
+    _say("xent 1024x32768")
+    z, t = dev_f32(inp.logits), dev_i32(inp.target)
+    loss, st, mean, inv, gb = _run_chain(z, t, -100, "bf16")
+    g = lmh.lmhead_xent_bwd(z, st, t, inv)
+    loss2, st2, mean2, inv2, gb2 = _run_chain(z, t, -100, "bf16")
+    assert torch.equal(st.view(torch.int32), st2.view(torch.int32))
+    assert torch.equal(gb.view(torch.int16), gb2.view(torch.int16))
+    assert torch.equal(mean.view(torch.int32), mean2.view(torch.int32))
+    assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
+    rows = np.array([0, 1, 255, 256, 511, 777, 1023])
+    st_ref = oracle.xent_fwd(inp.logits, inp.target, -100, rows=rows)
+    _check_stats(host_f32(st)[rows], st_ref)
+    ref_all = oracle.xent_fwd(inp.logits, inp.target, -100)
+    m_ref, inv_ref, _ = oracle.xent_mean(ref_all[:, 3], inp.target, -100)
+    assert_loss_close(host_f32(mean), [m_ref], 1e-5, "mean")
+    g_ref = oracle.xent_bwd(inp.logits, inp.target, -100, inv_ref, rows=rows)
+    _check_grad(host_f32(g)[rows], g_ref)
+
+
+def test_xent_131k_spikes_inplace():
+    """logits FP32 [8192 x 131072] ~ N(0, 3^2), 1% rows with a +30 spike, 2%
+    ignored: no inf/NaN anywhere; spike rows' m is the spike value; sampled
+    rows match the oracle; FP32 in-place == out-of-place bitwise; BF16 ==
+    RNE(FP32)."""
+    inp = workloads.xent_131k()
+    n, V = inp.logits.shape
+    _say("xent 8192x131072 spikes")
+    z = dev_f32(inp.logits)
+    t = dev_i32(inp.target)
+    loss, st, mean, inv, g = _run_chain(z, t, -100, "fp32")
+    sh = host_f32(st)
+    assert np.isfinite(sh).all() and np.isfinite(host_f32(loss)).all()
+    assert not torch.isnan(g).any().item() and not torch.isinf(g).any().item()
+    assert np.array_equal(_bits(sh[inp.spike_rows, 0]),
+                          _bits(inp.logits[inp.spike_rows, inp.spike_cols]))
+    ign = inp.meta["ignored_rows"]
+    rows = np.unique(np.concatenate([inp.spike_rows[:6], ign[:4], [0, 1, 4095, 4096, 8191]]))
+    st_ref = oracle.xent_fwd(inp.logits, inp.target, -100, rows=rows)
+    _check_stats(sh[rows], st_ref, "131k")
+    # mean over every row: oracle losses for all rows (FP64, one pass each)
+    ref_all = oracle.xent_fwd(inp.logits, inp.target, -100)
+    m_ref, inv_ref, nv = oracle.xent_mean(ref_all[:, 3], inp.target, -100)
+    assert nv == n - ign.size
+    assert_loss_close(host_f32(mean), [m_ref], 1e-5, "mean")
+    g_ref = oracle.xent_bwd(inp.logits, inp.target, -100, inv_ref, rows=rows)
+    gh = host_f32(g[torch.from_numpy(rows).cuda()])
+    _check_grad(gh, g_ref)
+    rs = np.abs(gh.astype(np.float64).sum(axis=1))
+    assert np.all(rs <= 1e-5 * float(host_f32(inv)[0]) + 1e-9)
+    gb = lmh.lmhead_xent_bwd(z, st, t, inv, grad_dtype="bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
+    del gb
+    # in place over the logits (the copy keeps z for nothing else)
+    zc = z.clone()
+    lmh.lmhead_xent_bwd(zc, st, t, inv, in_place=True)
+    torch.cuda.synchronize()
+    assert torch.equal(zc.view(torch.int32), g.view(torch.int32))

@@ -115,6 +115,13 @@ def integer_gemm(M: int, K: int, V: int, seed: int = SEED, lo: int = -8, hi: int
                       meta={"kind": "integer", "range": (lo, hi), "seed": seed})
 
 
+def integer_operands(shapes, seed: int = SEED, lo: int = -8, hi: int = 8):
+    """BF16 bit arrays of integers uniform in [lo, hi], drawn in the order of
+    `shapes` from one generator."""
+    rng = np.random.default_rng(seed)
+    return [int_to_bf16_bits(rng.integers(lo, hi + 1, tuple(s))) for s in shapes]
+
+
 def tiny_exact(seed: int = SEED) -> GemmInputs:
     """x [16 x 512], W [1024 x 512] integers in [-8, 8], targets in [0, 1024)."""
     g = integer_gemm(16, 512, 1024, seed)
