@@ -42,6 +42,35 @@ METRIC = "LM-head GEMM TFLOPS (% MFMA peak) + fused CE fwd+bwd GB/s (% HBM peak)
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch measured with rocprofv3 (FETCH_SIZE x 2.0 and
+# WRITE_SIZE x 1.0: the factors a plain 1 GiB device copy reads for these two
+# counters on this GPU), valid only for the kernel sources they were taken on
+# (code hash of the .hip file, see source_code_hash).  Changed code reports null.
+MEASURED_TRAFFIC = {
+    "logits_fp32": {"src": "gemm.hip", "sha": "d04147acb234bf09", "bytes": (786976 + 165324) * 1024},
+    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "7fa0ec9f59906b53",
+                          "bytes": (4195966 + 592 + 4113216 + 4194304) * 1024},
+}
+
+
+def source_code_hash(name):
+    """sha256 prefix of a kernel source with comments and whitespace removed,
+    so that edits to comments do not void a measurement."""
+    import hashlib
+    import re
+
+    with open(os.path.join(ROOT, "lm_head_fp32_amd", "csrc", name)) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
+def measured_traffic(key):
+    t = MEASURED_TRAFFIC[key]
+    return t["bytes"] if source_code_hash(t["src"]) == t["sha"] else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -56,6 +85,8 @@ def parse():
     ap.add_argument("--ce-rows", type=int, default=8192, help="rows of the large CE workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the side measurements")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -154,7 +185,8 @@ def main():
     for name in ("logits", "dgrad", "wgrad"):
         kern[name]["tflops"] = flop / (kern[name]["ms_mean"] * 1e-3) / 1e12
         kern[name]["frac_mfma_peak"] = kern[name]["tflops"] / PEAK_BF16_TFLOPS
-    ce_step_bytes = (4.0 * M * V + 24 * M) + ((4.0 + 2.0) * M * V + 24 * M)
+    n_valid_step = int((tgt != -100).sum().item())
+    ce_step_bytes = (4.0 * M * V + 24 * M) + (4.0 * n_valid_step * V + 2.0 * M * V + 24 * M)
     ce_step_ms = kern["xent_fwd"]["ms_mean"] + kern["xent_bwd"]["ms_mean"]
     kern["xent_fwd_bwd_bf16"] = {"gbps": ce_step_bytes / (ce_step_ms * 1e-3) / 1e9,
                                  "note": "logits (128 MiB) may sit in the 256 MB MALL here"}
@@ -189,7 +221,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(logits_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("logits_fp32"),
+            "algorithmic_bytes": int(2 * M * K + 2 * V * K + 4 * M * V),
         },
         "kernels": kern,
     }
@@ -243,8 +276,11 @@ def main():
         torch.cuda.synchronize()
         fwd_ms = statistics.median(ctm.ms("fwd"))
         bwd_ms = statistics.median(ctm.ms("bwd"))
+        # The backward writes every row but reads only rows whose target is
+        # not ignored (an ignored row's gradient is zero).
+        n_valid = int((ct != -100).sum().item())
         fwd_b = 4.0 * n_ce * v_ce + 24 * n_ce
-        bwd_b = 8.0 * n_ce * v_ce + 24 * n_ce
+        bwd_b = 4.0 * n_valid * v_ce + 4.0 * n_ce * v_ce + 24 * n_ce
         ce_gbps = (fwd_b + bwd_b) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9
         # BF16 gradients, then in place over a copy restored outside the timing
         gb = torch.empty((n_ce, v_ce), dtype=torch.bfloat16, device="cuda")
@@ -270,16 +306,29 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(ce_gbps / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("xent_fwd_bwd_fp32") if n_ce == 8192 else None,
+            "algorithmic_bytes": int(fwd_b + bwd_b),
             "fwd_ms_median": fwd_ms, "bwd_ms_median": bwd_ms,
             "fwd_gbps": fwd_b / (fwd_ms * 1e-3) / 1e9, "bwd_gbps": bwd_b / (bwd_ms * 1e-3) / 1e9,
             "bwd_bf16_ms_median": bwd16_ms,
-            "bwd_bf16_gbps": (6.0 * n_ce * v_ce + 24 * n_ce) / (bwd16_ms * 1e-3) / 1e9,
+            "bwd_bf16_gbps": (4.0 * n_valid * v_ce + 2.0 * n_ce * v_ce + 24 * n_ce)
+            / (bwd16_ms * 1e-3) / 1e9,
             "bwd_inplace_ms_median": bwdip_ms,
             "bwd_inplace_gbps": bwd_b / (bwdip_ms * 1e-3) / 1e9,
         }
         log(f"[bench] CE fwd {fwd_ms:.3f} ms bwd {bwd_ms:.3f} ms -> {ce_gbps:.0f} GB/s")
         del z, g32
+
+    # ------------------------------------------ counter calibration copy
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = nb
+        del src, dst
 
     # ------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:

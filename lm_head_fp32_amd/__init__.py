@@ -140,6 +140,17 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def _empty_rows(rows, cols, dtype, like):
+    """[rows, cols] output whose leading dimension is rounded up to the
+    library's alignment (4 elements for fp32, 8 for bf16); the padding
+    columns are never written."""
+    mult = 4 if dtype == torch.float32 else 8
+    ld = max((cols + mult - 1) // mult * mult, mult)
+    if ld == cols:
+        return torch.empty((rows, cols), dtype=dtype, device=like.device)
+    return torch.empty((rows, ld), dtype=dtype, device=like.device)[:, :cols]
+
+
 # --------------------------------------------------------------- the calls
 
 def lmhead_logits(x, W, out=None, out_dtype="fp32", stream=None):
@@ -155,7 +166,7 @@ def lmhead_logits(x, W, out=None, out_dtype="fp32", stream=None):
     if out is None:
         if code not in (LMH_BF16, LMH_FP32):
             _check("lmhead_logits", 1)
-        out = _empty((M, V), _TORCH_DT[code], x)
+        out = _empty_rows(M, V, _TORCH_DT[code], x)
     po, ldo = _mat(out, "out", out.dtype)
     if out.shape != (M, V):
         raise ValueError("out must be [M, V]")
@@ -221,7 +232,7 @@ def lmhead_xent_bwd(logits, stats, target, dloss, ignore_index=-100, dlogits=Non
     elif dlogits is None:
         if code not in (LMH_BF16, LMH_FP32):
             _check("lmhead_xent_bwd", 1)
-        dlogits = _empty((n, V), _TORCH_DT[code], logits)
+        dlogits = _empty_rows(n, V, _TORCH_DT[code], logits)
     pg, ldg = _mat(dlogits, "dlogits", dlogits.dtype)
     if dlogits.shape != (n, V):
         raise ValueError("dlogits must be [n, V]")
@@ -242,7 +253,7 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", stream=None):
     if dX is None:
         if code not in (LMH_BF16, LMH_FP32):
             _check("lmhead_dgrad", 1)
-        dX = _empty((M, K), _TORCH_DT[code], dlogits)
+        dX = _empty_rows(M, K, _TORCH_DT[code], dlogits)
     px, ldx = _mat(dX, "dX", dX.dtype)
     if dX.shape != (M, K):
         raise ValueError("dX must be [M, K]")
@@ -262,7 +273,7 @@ def lmhead_wgrad(dlogits, x, dW=None, accumulate=False, stream=None):
     if dW is None:
         if accumulate:
             raise ValueError("accumulate=True needs an existing dW")
-        dW = _empty((V, K), torch.float32, dlogits)
+        dW = _empty_rows(V, K, torch.float32, dlogits)
     pw, ldw = _mat(dW, "dW", torch.float32)
     if dW.shape != (V, K):
         raise ValueError("dW must be [V, K]")

@@ -1,30 +1,33 @@
-// gemm.hip -- BF16 x BF16 -> FP32 contraction on gfx950 matrix cores.
+// gemm.hip -- BF16 x BF16 -> FP32 contractions on gfx950 matrix cores.
 //
-// One kernel template serves the three GEMMs of the LM head:
-//   logits  out[m][v]  = sum_k x[m][k] W[v][k]     (R = V, C = M, P = K)
-//   dgrad   dX[m][k]   = sum_v dl[m][v] W[v][k]    (R = K, C = M, P = V)
+// The three GEMMs of the LM head, all as D[c][r] = sum_p A(r, p) B(c, p)
+// with r the output's contiguous dimension:
+//   logits  out[m][v]   = sum_k x[m][k] W[v][k]    (R = V, C = M, P = K)
+//   dgrad   dX[m][k]    = sum_v dl[m][v] W[v][k]   (R = K, C = M, P = V)
 //   wgrad   dW[v][k] (+)= sum_m dl[m][v] x[m][k]   (R = K, C = V, P = M)
 // The logits GEMM keeps the FP32 accumulator as the FP32 output, or rounds
 // it to BF16 for the legacy comparison (Megatron-LM "Add mixed-precision
 // (FP32) LM output logits", section "What does this PR do?").
 //
-// Orientation: the kernel computes D^T tiles with the matrix-core "row"
-// dimension on R, the output's contiguous dimension.  A 32x32 MFMA leaves
-// four consecutive rows of one column in each lane, so every lane stores 16
-// contiguous bytes of an output row with no LDS round trip.
+// Orientation: tiles are computed with the matrix-core "row" dimension on R.
+// A 32x32 MFMA leaves four consecutive rows of one column in each lane, so
+// every lane stores 16 contiguous bytes of an output row with no LDS trip.
 //
-// Data movement per workgroup and K-stage (BK = 64 contraction elements):
-//   global -> registers (16-byte loads, coalesced along the contiguous dim)
-//   registers -> LDS, laid out [row][p] with a 16-byte pad per row so the
-//   32 rows read by one MFMA operand fetch fall in distinct bank groups;
-//   operands stored p-major in HBM (dgrad's W, wgrad's x and dl) are loaded
-//   as 8x8 blocks and transposed in registers before the LDS write.
-//   LDS is double buffered: the next stage's global loads are in flight
-//   while the current stage feeds the MFMAs.
-// Workgroup -> tile mapping: consecutive workgroup ids are dealt round-robin
-// to the 8 XCDs; ids are regrouped so that the tiles one XCD runs at the same
-// time share operand strips in that XCD's L2.
+// Two kernels:
+//  * gemm_nt_big -- the logits GEMM (both operands keep P contiguous):
+//    256 x 256 tiles, 8 waves, operand stages loaded straight into LDS by
+//    buffer loads, XOR-swizzled LDS rows, software-pipelined MFMA loop (see
+//    the comments at the kernel).
+//  * gemm_kernel -- the generic form used by dgrad and wgrad, whose operands
+//    may be stored p-major: 128 x 128 tiles, register-staged double buffer,
+//    p-major operands loaded as 8x8 blocks and transposed in registers
+//    before the LDS write (LDS rows padded by 16 bytes).
+// Workgroup -> tile mapping: the hardware deals consecutive workgroup ids
+// round-robin to the 8 XCDs; ids are regrouped so that the tiles one XCD runs
+// at the same time share operand strips in that XCD's L2.
 #include "common.h"
+
+#include <algorithm>
 
 namespace lmh {
 namespace {
@@ -333,6 +336,362 @@ __global__ __launch_bounds__(WR * WC * 64) void gemm_kernel(GemmProblem g, TileM
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel for the logits GEMM, where both operands keep the
+// contraction dimension contiguous (W [V][K], x [M][K]).
+//
+// Workgroup tile BR x BC (R = vocabulary, C = tokens), WR x WC waves, each
+// wave owning a TR x TC block of 32x32 accumulators held in AGPRs (128 x 128
+// per wave: 256 accumulator registers, one wave per SIMD).  A larger wave
+// tile halves the LDS bytes read per MFMA compared with 64 x 64 wave tiles.
+// LDS holds [row][BK] BF16 with 16-byte chunks XOR-swizzled by row so that
+// both the staging writes and the MFMA fragment reads touch distinct banks
+// for any 8 (32-bank) or 16 (64-bank) consecutive lanes.  Global loads for
+// stage k+2 are issued as soon as stage k+1 has been written to LDS and
+// overlap the whole MFMA phase of stage k+1.
+template <int BK>
+__device__ __forceinline__ int lds_swz(int row)
+{
+    static_assert(BK == 64, "swizzle defined for 128-byte rows");
+    return (row + (row >> 3)) & 7;
+}
+
+__device__ __forceinline__ void lds_barrier()
+{
+    // LDS writes of this wave are complete, then the workgroup barrier; the
+    // "memory" clobber keeps the compiler from moving LDS accesses across it.
+    // Outstanding global loads (the next stage's prefetch) are not waited on.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x8;
+constexpr int kSgVmemRead = 0x20;
+constexpr int kSgDsRead = 0x100;
+constexpr int kSgDsWrite = 0x200;
+
+// Buffer resource over one operand tile: base = the tile's first row, range
+// checking off in practice (2^31 - 1 bytes); word 3 is the raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base)
+{
+    // The base is the same for the whole workgroup; say so, so that the
+    // descriptor lives in scalar registers.
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    void *u = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff)
+{
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
+    return *reinterpret_cast<uint4 *>(&v);
+}
+
+#define LMH_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+template <int BR, int BC, int BK, int WR, int WC, int EPI>
+__global__ void __launch_bounds__(WR * WC * 64)
+    __attribute__((amdgpu_waves_per_eu(WR * WC / 4, WR * WC / 4)))
+gemm_nt_big(GemmProblem g, TileMap tm)
+{
+    constexpr int NT = WR * WC * 64;
+    constexpr int NW = WR * WC;
+    constexpr int TR = BR / WR, TC = BC / WC;
+    constexpr int FR = TR / 32, FC = TC / 32;
+    constexpr int KCH = BK / 8;  // 16-byte chunks per LDS row
+    constexpr int CA = BR * KCH / NT, CB = BC * KCH / NT;
+    constexpr int NKK = BK / 16;
+    // Direct loads: one wave instruction moves 64 x 16 B = 1 KiB = 1024/(2*BK)
+    // tile rows into LDS.
+    constexpr int ROWS_PER_KB = 1024 / (2 * BK);
+    constexpr int NBA = BR / ROWS_PER_KB / NW, NBB = BC / ROWS_PER_KB / NW;
+    static_assert((BR * KCH) % NT == 0 && (BC * KCH) % NT == 0, "tile/threads mismatch");
+    static_assert(NKK == 4 && FR % 2 == 0, "schedule written for four 16-wide k steps");
+    static_assert(NBA * NW * ROWS_PER_KB == BR && NBB * NW * ROWS_PER_KB == BC, "DMA split");
+
+    // Two stages per operand as separate arrays, so that the compiler can tell
+    // a direct load into one stage from the fragment reads of the other.
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[BR * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA1[BR * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[BC * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB1[BC * BK];
+
+    int tr, tc;
+    map_tile(tm, tr, tc);
+    const int64_t r0 = static_cast<int64_t>(tr) * BR;
+    const int64_t c0 = static_cast<int64_t>(tc) * BC;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wr = wave % WR;
+    const int wc = wave / WR;
+
+    const uint16_t *baseA = g.A + r0 * g.lda;
+    const uint16_t *baseB = g.B + c0 * g.ldb;
+    const __amdgpu_buffer_rsrc_t rsA = tile_rsrc(baseA);
+    const __amdgpu_buffer_rsrc_t rsB = tile_rsrc(baseB);
+
+    // Direct global -> LDS loads (steady state).  Wave w fills KiB blocks
+    // w*NB .. w*NB+NB-1 of each operand stage; lane l of a block lands at
+    // byte 16*l, i.e. tile row ROWS_PER_KB*b + l/KCH, LDS slot l%KCH, which
+    // holds chunk (l%KCH) ^ swz(row).  Rows past R (or C) read the last valid
+    // row: their products only reach outputs that are never stored.
+    uint32_t da[NBA], db[NBB];
+#pragma unroll
+    for (int i = 0; i < NBA; ++i) {
+        const int row = (wave * NBA + i) * ROWS_PER_KB + lane / KCH;
+        const int64_t gr = min(r0 + row, g.R - 1) - r0;
+        const int kc = (lane % KCH) ^ lds_swz<BK>(row);
+        da[i] = static_cast<uint32_t>((gr * g.lda + kc * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NBB; ++i) {
+        const int row = (wave * NBB + i) * ROWS_PER_KB + lane / KCH;
+        const int64_t gr = min(c0 + row, g.C - 1) - c0;
+        const int kc = (lane % KCH) ^ lds_swz<BK>(row);
+        db[i] = static_cast<uint32_t>((gr * g.ldb + kc * 8) * 2);
+    }
+    auto dma_a = [&](uint16_t *lds, int64_t p0, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsA, LMH_LDS_PTR(lds + (wave * NBA + i) * 512), 16, static_cast<int>(da[i]),
+            static_cast<int>(p0 * 2), 0, 0);
+    };
+    auto dma_b = [&](uint16_t *lds, int64_t p0, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsB, LMH_LDS_PTR(lds + (wave * NBB + i) * 512), 16, static_cast<int>(db[i]),
+            static_cast<int>(p0 * 2), 0, 0);
+    };
+
+    // Register-staged loads (prologue of a short P and the ragged tail stage).
+    constexpr int RSTEP = NT / KCH;  // tile rows between a thread's chunks
+    static_assert(RSTEP % 8 == 0, "swizzle key must repeat across chunks");
+    const int crow = tid / KCH, ccol = tid % KCH;
+    auto staged_load = [&](uint16_t *lA, uint16_t *lB, int64_t p0) {
+        const int64_t gp = p0 + ccol * 8;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int row = crow + i * RSTEP;
+            const uint16_t *src = baseA + (min(r0 + row, g.R - 1) - r0) * g.lda + gp;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (gp + 8 <= g.P)
+                v = load16(src);
+            else if (gp < g.P)
+                v = load_partial(src, static_cast<int>(g.P - gp));
+            *reinterpret_cast<uint4 *>(&lA[row * BK + ((ccol ^ lds_swz<BK>(row)) * 8)]) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int row = crow + i * RSTEP;
+            const uint16_t *src = baseB + (min(c0 + row, g.C - 1) - c0) * g.ldb + gp;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (gp + 8 <= g.P)
+                v = load16(src);
+            else if (gp < g.P)
+                v = load_partial(src, static_cast<int>(g.P - gp));
+            *reinterpret_cast<uint4 *>(&lB[row * BK + ((ccol ^ lds_swz<BK>(row)) * 8)]) = v;
+        }
+    };
+
+    // Per-lane fragment addressing.  Fragment i of a wave covers tile rows
+    // wr*TR + 32i + (lane%32); the XOR key of its chunk index (lane/32 is the
+    // lane's half of the 16-wide k step) depends on i only through its parity.
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    const int fbA = (wr * TR + lrow) * BK;
+    const int fbB = (wc * TC + lrow) * BK;
+    int keyA[2], keyB[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        keyA[par] = khalf ^ lds_swz<BK>(wr * TR + par * 32 + lrow);
+        keyB[par] = khalf ^ lds_swz<BK>(wc * TC + par * 32 + lrow);
+    }
+    bf16x8 fa[2][FR], fb[2][FC];
+    auto frag_load = [&](const uint16_t *lA, const uint16_t *lB, int kk, int slot) {
+        const int ka0 = ((2 * kk) ^ keyA[0]) * 8, ka1 = ((2 * kk) ^ keyA[1]) * 8;
+        const int kb0 = ((2 * kk) ^ keyB[0]) * 8, kb1 = ((2 * kk) ^ keyB[1]) * 8;
+#pragma unroll
+        for (int i = 0; i < FR; ++i)
+            fa[slot][i] = *reinterpret_cast<const bf16x8 *>(
+                &lA[fbA + i * 32 * BK + ((i & 1) ? ka1 : ka0)]);
+#pragma unroll
+        for (int j = 0; j < FC; ++j)
+            fb[slot][j] = *reinterpret_cast<const bf16x8 *>(
+                &lB[fbB + j * 32 * BK + ((j & 1) ? kb1 : kb0)]);
+    };
+
+    f32x16 acc[FR][FC];
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FC; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+    auto mfma_rows = [&](int slot, int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < FC; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
+                                                                    acc[i][j], 0, 0, 0);
+    };
+
+    // One steady-state stage: compute stage kt from (cA, cB) while stage
+    // kt+1 (wholly inside P) streams straight into (nA, nB).  Fragment reads
+    // run one k step ahead of the MFMAs; the direct loads are spread over the
+    // first k step; the workgroup barrier (after this wave's direct loads have
+    // landed) sits halfway through the last k step so the first fragment
+    // reads of stage kt+1 are covered by the remaining MFMAs.
+    auto stage_dma = [&](const uint16_t *cA, const uint16_t *cB, uint16_t *nA, uint16_t *nB,
+                         int64_t kt) {
+        const int64_t p1 = (kt + 1) * BK;
+#pragma unroll
+        for (int i = 0; i < NBA; ++i)
+            dma_a(nA, p1, i);
+#pragma unroll
+        for (int i = 0; i < NBB; ++i)
+            dma_b(nB, p1, i);
+        frag_load(cA, cB, 1, 1);
+        mfma_rows(0, 0, FR);
+        frag_load(cA, cB, 2, 0);
+        mfma_rows(1, 0, FR);
+        frag_load(cA, cB, 3, 1);
+        mfma_rows(0, 0, FR);
+        mfma_rows(1, 0, FR / 2);
+        constexpr int nmf = FR * FC;
+        constexpr int nrd = FR + FC;
+        constexpr int ndma = NBA + NBB;
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+#pragma unroll
+            for (int m = 0; m < nmf; ++m) {
+                if (s == 0 && m < ndma)
+                    __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                if (m < nrd)
+                    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, nmf / 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        frag_load(nA, nB, 0, 0);
+        mfma_rows(1, FR / 2, FR);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, nrd, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, nmf / 2, 0);
+    };
+
+    const int64_t nk = (g.P + BK - 1) / BK;
+    const int64_t nfull = g.P / BK;
+    int64_t kt = 0;
+    if (nk > 0) {
+        if (nfull > 0) {
+#pragma unroll
+            for (int i = 0; i < NBA; ++i)
+                dma_a(sA0, 0, i);
+#pragma unroll
+            for (int i = 0; i < NBB; ++i)
+                dma_b(sB0, 0, i);
+        } else {
+            staged_load(sA0, sB0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        frag_load(sA0, sB0, 0, 0);
+    }
+    for (; kt + 2 < nfull; kt += 2) {
+        stage_dma(sA0, sB0, sA1, sB1, kt);
+        stage_dma(sA1, sB1, sA0, sB0, kt + 1);
+    }
+    if (kt + 1 < nfull) {
+        stage_dma(sA0, sB0, sA1, sB1, kt);
+        ++kt;
+    }
+    // Drain: the last full stage and the ragged tail (register-staged).
+    for (; kt < nk; ++kt) {
+        uint16_t *cA = (kt & 1) ? sA1 : sA0;
+        uint16_t *cB = (kt & 1) ? sB1 : sB0;
+        uint16_t *nA = (kt & 1) ? sA0 : sA1;
+        uint16_t *nB = (kt & 1) ? sB0 : sB1;
+        frag_load(cA, cB, 1, 1);
+        mfma_rows(0, 0, FR);
+        frag_load(cA, cB, 2, 0);
+        mfma_rows(1, 0, FR);
+        frag_load(cA, cB, 3, 1);
+        mfma_rows(0, 0, FR);
+        mfma_rows(1, 0, FR);
+        if (kt + 1 < nk)
+            staged_load(nA, nB, (kt + 1) * BK);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kt + 1 < nk)
+            frag_load(nA, nB, 0, 0);
+    }
+
+    // Epilogue: lane l, register 4q+e of a 32x32 tile = row 8q + 4(l/32) + e,
+    // column l%32; four consecutive R values per lane -> one 16-byte store.
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+#pragma unroll
+        for (int j = 0; j < FC; ++j) {
+            const int64_t c = c0 + wc * TC + j * 32 + (lane & 31);
+            if (c >= g.C)
+                continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = r0 + wr * TR + i * 32 + q * 8 + (lane >> 5) * 4;
+                if (r >= g.R)
+                    continue;
+                const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                const bool full = r + 4 <= g.R;
+                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
+                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
+                    if (full) {
+                        uint2 w;
+                        w.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+                        w.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+                        *reinterpret_cast<uint2 *>(out) = w;
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e)
+                            out[e] = static_cast<uint16_t>(f32_to_bf16_bits(vv[e]));
+                    }
+                } else {
+                    float *out = static_cast<float *>(g.D) + c * g.ldd + r;
+                    if (full) {
+                        *reinterpret_cast<float4 *>(out) = make_float4(v0, v1, v2, v3);
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e)
+                            out[e] = vv[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int BR, int BC, int WR, int WC>
+hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
+{
+    constexpr int BK = 64;
+    TileMap tm;
+    tm.tiles_r = static_cast<int>((p.R + BR - 1) / BR);
+    tm.tiles_c = static_cast<int>((p.C + BC - 1) / BC);
+    tm.group_r = group_r < 1 ? 1 : group_r;
+    const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
+    if (nwg == 0)
+        return hipSuccess;
+    dim3 grid(static_cast<unsigned>(nwg)), block(WR * WC * 64);
+    if (epi == Epi::kStoreBF16)
+        hipLaunchKernelGGL((gemm_nt_big<BR, BC, BK, WR, WC, 1>), grid, block, 0, s, p, tm);
+    else
+        hipLaunchKernelGGL((gemm_nt_big<BR, BC, BK, WR, WC, 0>), grid, block, 0, s, p, tm);
+    return hipGetLastError();
+}
+
 template <int BR, int BC, int WR, int WC, bool AT, bool BT>
 hipError_t launch_cfg(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
@@ -363,10 +722,14 @@ hipError_t launch_cfg(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 
 hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 {
-    // R = V (vocabulary), C = M (tokens).
-    if (p.C <= 32)
-        return launch_cfg<128, 32, 4, 1, false, false>(p, epi, 8, s);
-    return launch_cfg<128, 128, 2, 2, false, false>(p, epi, 8, s);
+    // R = V (vocabulary), C = M (tokens).  The large-tile kernel addresses a
+    // tile through 32-bit byte offsets: keep its span below 2^31 bytes.
+    const bool offsets_fit = (256 * std::max(p.lda, p.ldb) + 64) * 2 < (int64_t(1) << 31);
+    if (!offsets_fit)
+        return launch_cfg<128, 128, 2, 2, false, false>(p, epi, 8, s);
+    if (p.C <= 128)
+        return launch_big<128, 128, 2, 2>(p, epi, 8, s);
+    return launch_big<256, 256, 4, 2>(p, epi, 8, s);
 }
 
 hipError_t launch_gemm_dgrad(const GemmProblem &p, Epi epi, hipStream_t s)
