@@ -47,9 +47,9 @@ PEAK_HBM_GBS = 8000.0
 # counters on this GPU), valid only for the kernel sources they were taken on
 # (code hash of the .hip file, see source_code_hash).  Changed code reports null.
 MEASURED_TRAFFIC = {
-    "logits_fp32": {"src": "gemm.hip", "sha": "d04147acb234bf09", "bytes": (786976 + 165324) * 1024},
+    "logits_fp32": {"src": "gemm.hip", "sha": "f8518ce4a6e8440a", "bytes": (2 * 393555 + 166595) * 1024},
     "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "7fa0ec9f59906b53",
-                          "bytes": (4195966 + 592 + 4113216 + 4194304) * 1024},
+                          "bytes": (2 * 2097981 + 592 + 2 * 2056605 + 4194304) * 1024},
 }
 
 
@@ -335,25 +335,30 @@ def main():
         import oracle
 
         thr = oracle.default_threads()
-        rows = np.arange(0, M, max(1, M // (4 * thr)))[: 4 * thr]
+        # Bounded samples of the same work (a few seconds each): logits rows
+        # of the step workload, and rows of the 8192 x 131072 CE workload.
+        n_rows = min(M, 32 * thr)
+        rows = np.linspace(0, M - 1, n_rows).astype(np.int64)
         log(f"[bench] cpu baseline: oracle logits on {rows.size} of {M} rows, {thr} threads")
         t0 = time.perf_counter()
         oracle.logits(inp.x, inp.W, rows=rows, with_abs=False, nthreads=thr)
         dt = time.perf_counter() - t0
         cpu_tflops = 2.0 * rows.size * K * V / dt / 1e12
-        n_cpu = 4 * thr
+        n_cpu = min(8192, 64 * thr)
         ce = workloads.xent_logits(n_cpu, 131072, sigma=3.0, spike_frac=0.01, spike=30.0,
                                    ignore_frac=0.02, seed=workloads.SEED)
+        log(f"[bench] cpu baseline: oracle CE fwd+bwd on {n_cpu} rows x 131072")
         t0 = time.perf_counter()
         st = oracle.xent_fwd(ce.logits, ce.target, -100, nthreads=thr)
-        _, inv_ref, _ = oracle.xent_mean(st[:, 3], ce.target, -100)
+        _, inv_ref, nv = oracle.xent_mean(st[:, 3], ce.target, -100)
         oracle.xent_bwd(ce.logits, ce.target, -100, inv_ref, nthreads=thr)
         dtc = time.perf_counter() - t0
-        cpu_ce = (12.0 * n_cpu * 131072 + 48 * n_cpu) / dtc / 1e9
+        cpu_ce = (4.0 * n_cpu * 131072 + 24 * n_cpu + 4.0 * nv * 131072 + 4.0 * n_cpu * 131072
+                  + 24 * n_cpu) / dtc / 1e9
         out["cpu_baseline"] = {
             "value": round(cpu_tflops, 6), "unit": "TFLOPS", "cores": thr, "kind": "oracle",
             "sample": f"FP64 oracle logits GEMM on {rows.size} of {M} rows (K={K}, V={V}), "
-                      f"{dt:.2f} s; CE fwd+bwd on {n_cpu} rows x 131072, {dtc:.2f} s",
+                      f"{dt:.2f} s; CE fwd+bwd on {n_cpu} of 8192 rows x 131072, {dtc:.2f} s",
             "ce_gbps": round(cpu_ce, 4),
         }
         log(f"[bench] cpu baseline {cpu_tflops * 1e3:.2f} GFLOPS, CE {cpu_ce:.3f} GB/s")

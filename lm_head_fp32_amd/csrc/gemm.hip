@@ -28,6 +28,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace lmh {
 namespace {
@@ -391,28 +392,193 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 #define LMH_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-template <int BR, int BC, int BK, int WR, int WC, int EPI>
+// ---------------------------------------------------------------------------
+// Operand loaders of gemm_big.  Both fill the same LDS layout: [row][BK] BF16,
+// 16-byte chunks XOR-swizzled by row (lds_swz), so the MFMA fragment reads
+// are identical whichever way an operand is stored in memory.
+
+// An operand stored [rows][P] (contraction contiguous): each wave instruction
+// moves 1 KiB (1024 / (2 BK) rows) straight from memory into LDS.
+template <int ROWS, int BK, int NW>
+struct DmaOperand {
+    static constexpr int KCH = BK / 8;
+    static constexpr int ROWS_PER_KB = 1024 / (2 * BK);
+    static constexpr int NB = ROWS / ROWS_PER_KB / NW;  // direct loads per wave per stage
+    static constexpr int W = 0;                           // no register transpose
+    static_assert(NB * NW * ROWS_PER_KB == ROWS, "DMA split");
+    __amdgpu_buffer_rsrc_t rs;
+    const uint16_t *base;  // first row of the tile
+    int64_t ld, row0, nrows, P;
+    uint32_t off[NB];
+
+    __device__ __forceinline__ void init(const uint16_t *g, int64_t ld_, int64_t row0_,
+                                         int64_t nrows_, int64_t P_, int wave, int lane)
+    {
+        ld = ld_, row0 = row0_, nrows = nrows_, P = P_;
+        base = g + row0 * ld;
+        rs = tile_rsrc(base);
+        // Lane l of block b lands at byte 16 l: tile row ROWS_PER_KB*b + l/KCH,
+        // LDS slot l%KCH, which holds chunk (l%KCH) ^ swz(row).  Rows past the
+        // edge read the last valid row (never stored).
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int row = (wave * NB + i) * ROWS_PER_KB + lane / KCH;
+            const int64_t gr = min(row0 + row, nrows - 1) - row0;
+            const int kc = (lane % KCH) ^ lds_swz<BK>(row);
+            off[i] = static_cast<uint32_t>((gr * ld + kc * 8) * 2);
+        }
+    }
+    __device__ __forceinline__ void dma(uint16_t *lds, int64_t p0, int wave)
+    {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, LMH_LDS_PTR(lds + (wave * NB + i) * 512), 16, static_cast<int>(off[i]),
+                static_cast<int>(p0 * 2), 0, 0);
+    }
+    // Guarded register path (ragged tail stage, edge tiles): zero past P.
+    template <int NT>
+    __device__ __forceinline__ void staged(uint16_t *lds, int64_t p0, int tid)
+    {
+        constexpr int RSTEP = NT / KCH;
+        const int crow = tid / KCH, ccol = tid % KCH;
+        const int64_t gp = p0 + ccol * 8;
+#pragma unroll
+        for (int i = 0; i < ROWS / RSTEP; ++i) {
+            const int row = crow + i * RSTEP;
+            const uint16_t *src = base + (min(row0 + row, nrows - 1) - row0) * ld + gp;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (gp + 8 <= P)
+                v = load16(src);
+            else if (gp < P)
+                v = load_partial(src, static_cast<int>(P - gp));
+            *reinterpret_cast<uint4 *>(&lds[row * BK + ((ccol ^ lds_swz<BK>(row)) * 8)]) = v;
+        }
+    }
+};
+
+// An operand stored [P][rows] (rows contiguous): every thread owns one block
+// of 8 contraction rows x W tile rows, loads it (W*2 bytes per contraction
+// row), transposes it in registers and writes W 16-byte LDS chunks.
+template <int ROWS, int BK, int NT>
+struct TransOperand {
+    static constexpr int W = ROWS * BK / 8 / NT;  // tile rows per block
+    static constexpr int RG = ROWS / W;           // blocks along the rows
+    static constexpr int NB = 0;                  // no direct loads
+    static_assert(W == 2 || W == 4 || W == 8, "block width");
+    static_assert(RG * (BK / 8) == NT, "one block per thread");
+    typedef uint32_t chunk_t __attribute__((ext_vector_type(W / 2)));
+    chunk_t v[8];
+    const uint16_t *base;  // column row0 of the operand
+    int64_t ld, row0, nrows, P;
+    int pg, rg;
+    uint32_t voff;
+
+    __device__ __forceinline__ void init(const uint16_t *g, int64_t ld_, int64_t row0_,
+                                         int64_t nrows_, int64_t P_, int tid)
+    {
+        ld = ld_, row0 = row0_, nrows = nrows_, P = P_;
+        base = g + row0;
+        pg = tid / RG;
+        rg = tid % RG;
+        voff = static_cast<uint32_t>((static_cast<int64_t>(pg) * 8 * ld + rg * W) * 2);
+    }
+    __device__ __forceinline__ chunk_t bload(__amdgpu_buffer_rsrc_t r, int soff) const
+    {
+        if constexpr (W == 8) {
+            auto x = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
+            return *reinterpret_cast<chunk_t *>(&x);
+        } else if constexpr (W == 4) {
+            auto x = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), soff, 0);
+            return *reinterpret_cast<chunk_t *>(&x);
+        } else {
+            auto x = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), soff, 0);
+            return *reinterpret_cast<chunk_t *>(&x);
+        }
+    }
+    // Stage wholly inside P and tile wholly inside the rows.
+    __device__ __forceinline__ void load_fast(int64_t p0)
+    {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(base + p0 * ld);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = bload(r, static_cast<int>(e * ld * 2));
+    }
+    __device__ __forceinline__ void load_guarded(int64_t p0)
+    {
+        const int64_t gr = row0 + rg * W;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t gp = p0 + pg * 8 + e;
+            uint16_t t[W];
+#pragma unroll
+            for (int j = 0; j < W; ++j)
+                t[j] = 0;
+            if (gp < P) {
+                const uint16_t *src = base + gp * ld + rg * W;
+#pragma unroll
+                for (int j = 0; j < W; ++j)
+                    if (gr + j < nrows)
+                        t[j] = src[j];
+            }
+#pragma unroll
+            for (int h = 0; h < W / 2; ++h)
+                v[e][h] = static_cast<uint32_t>(t[2 * h]) | (static_cast<uint32_t>(t[2 * h + 1]) << 16);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *lds) const
+    {
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int h = j >> 1;
+            uint4 o;
+            if (j & 1) {
+                o = make_uint4(hi_pair(v[0][h], v[1][h]), hi_pair(v[2][h], v[3][h]),
+                               hi_pair(v[4][h], v[5][h]), hi_pair(v[6][h], v[7][h]));
+            } else {
+                o = make_uint4(lo_pair(v[0][h], v[1][h]), lo_pair(v[2][h], v[3][h]),
+                               lo_pair(v[4][h], v[5][h]), lo_pair(v[6][h], v[7][h]));
+            }
+            const int row = rg * W + j;
+            *reinterpret_cast<uint4 *>(&lds[row * BK + ((pg ^ lds_swz<BK>(row)) * 8)]) = o;
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// gemm_big: BR x BC tiles, WR x WC waves (two per SIMD with 8 waves), BK = 64.
+// Operands whose contraction dimension is contiguous stream into LDS by
+// direct buffer loads; p-major operands (dgrad's W, wgrad's x and dlogits)
+// go through registers and an 8 x W transpose.  Two LDS stages per operand
+// as separate arrays, so that the compiler can tell a direct load into one
+// stage from the fragment reads of the other (the steady loop is unrolled by
+// two to keep the stage choice compile-time).
+//
+// Steady state (interior tile, full stages), per stage kt:
+//   top:   direct loads of stage kt+1 into the other stage (spread over the
+//          first 16-wide k step, one per MFMA);
+//   k0-2:  fragment reads one k step ahead of the MFMAs;
+//   k2:    transposed operands: stage kt+1 (loaded into registers one stage
+//          earlier) is written to the other stage, then stage kt+2 is loaded;
+//   k3:    half the MFMAs, the workgroup barrier (after this wave's direct
+//          loads landed), the first fragment reads of stage kt+1, the other
+//          half of the MFMAs -- the barrier and the read latency hide behind
+//          matrix work.
+// Edge tiles and the last stages run a guarded loop with the same layout.
+template <int BR, int BC, int BK, int WR, int WC, bool AT, bool BT, int EPI>
 __global__ void __launch_bounds__(WR * WC * 64)
     __attribute__((amdgpu_waves_per_eu(WR * WC / 4, WR * WC / 4)))
-gemm_nt_big(GemmProblem g, TileMap tm)
+gemm_big(GemmProblem g, TileMap tm)
 {
     constexpr int NT = WR * WC * 64;
     constexpr int NW = WR * WC;
     constexpr int TR = BR / WR, TC = BC / WC;
     constexpr int FR = TR / 32, FC = TC / 32;
-    constexpr int KCH = BK / 8;  // 16-byte chunks per LDS row
-    constexpr int CA = BR * KCH / NT, CB = BC * KCH / NT;
     constexpr int NKK = BK / 16;
-    // Direct loads: one wave instruction moves 64 x 16 B = 1 KiB = 1024/(2*BK)
-    // tile rows into LDS.
-    constexpr int ROWS_PER_KB = 1024 / (2 * BK);
-    constexpr int NBA = BR / ROWS_PER_KB / NW, NBB = BC / ROWS_PER_KB / NW;
-    static_assert((BR * KCH) % NT == 0 && (BC * KCH) % NT == 0, "tile/threads mismatch");
-    static_assert(NKK == 4 && FR % 2 == 0, "schedule written for four 16-wide k steps");
-    static_assert(NBA * NW * ROWS_PER_KB == BR && NBB * NW * ROWS_PER_KB == BC, "DMA split");
+    static_assert(BK == 64 && NKK == 4 && FR % 2 == 0, "schedule written for BK = 64");
+    using OpA = std::conditional_t<AT, TransOperand<BR, BK, NT>, DmaOperand<BR, BK, NW>>;
+    using OpB = std::conditional_t<BT, TransOperand<BC, BK, NT>, DmaOperand<BC, BK, NW>>;
 
-    // Two stages per operand as separate arrays, so that the compiler can tell
-    // a direct load into one stage from the fragment reads of the other.
     __shared__ __attribute__((aligned(16))) uint16_t sA0[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB0[BC * BK];
@@ -427,72 +593,18 @@ gemm_nt_big(GemmProblem g, TileMap tm)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int wr = wave % WR;
     const int wc = wave / WR;
+    const bool interior = (r0 + BR <= g.R) && (c0 + BC <= g.C);
 
-    const uint16_t *baseA = g.A + r0 * g.lda;
-    const uint16_t *baseB = g.B + c0 * g.ldb;
-    const __amdgpu_buffer_rsrc_t rsA = tile_rsrc(baseA);
-    const __amdgpu_buffer_rsrc_t rsB = tile_rsrc(baseB);
-
-    // Direct global -> LDS loads (steady state).  Wave w fills KiB blocks
-    // w*NB .. w*NB+NB-1 of each operand stage; lane l of a block lands at
-    // byte 16*l, i.e. tile row ROWS_PER_KB*b + l/KCH, LDS slot l%KCH, which
-    // holds chunk (l%KCH) ^ swz(row).  Rows past R (or C) read the last valid
-    // row: their products only reach outputs that are never stored.
-    uint32_t da[NBA], db[NBB];
-#pragma unroll
-    for (int i = 0; i < NBA; ++i) {
-        const int row = (wave * NBA + i) * ROWS_PER_KB + lane / KCH;
-        const int64_t gr = min(r0 + row, g.R - 1) - r0;
-        const int kc = (lane % KCH) ^ lds_swz<BK>(row);
-        da[i] = static_cast<uint32_t>((gr * g.lda + kc * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < NBB; ++i) {
-        const int row = (wave * NBB + i) * ROWS_PER_KB + lane / KCH;
-        const int64_t gr = min(c0 + row, g.C - 1) - c0;
-        const int kc = (lane % KCH) ^ lds_swz<BK>(row);
-        db[i] = static_cast<uint32_t>((gr * g.ldb + kc * 8) * 2);
-    }
-    auto dma_a = [&](uint16_t *lds, int64_t p0, int i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsA, LMH_LDS_PTR(lds + (wave * NBA + i) * 512), 16, static_cast<int>(da[i]),
-            static_cast<int>(p0 * 2), 0, 0);
-    };
-    auto dma_b = [&](uint16_t *lds, int64_t p0, int i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsB, LMH_LDS_PTR(lds + (wave * NBB + i) * 512), 16, static_cast<int>(db[i]),
-            static_cast<int>(p0 * 2), 0, 0);
-    };
-
-    // Register-staged loads (prologue of a short P and the ragged tail stage).
-    constexpr int RSTEP = NT / KCH;  // tile rows between a thread's chunks
-    static_assert(RSTEP % 8 == 0, "swizzle key must repeat across chunks");
-    const int crow = tid / KCH, ccol = tid % KCH;
-    auto staged_load = [&](uint16_t *lA, uint16_t *lB, int64_t p0) {
-        const int64_t gp = p0 + ccol * 8;
-#pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            const int row = crow + i * RSTEP;
-            const uint16_t *src = baseA + (min(r0 + row, g.R - 1) - r0) * g.lda + gp;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gp + 8 <= g.P)
-                v = load16(src);
-            else if (gp < g.P)
-                v = load_partial(src, static_cast<int>(g.P - gp));
-            *reinterpret_cast<uint4 *>(&lA[row * BK + ((ccol ^ lds_swz<BK>(row)) * 8)]) = v;
-        }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int row = crow + i * RSTEP;
-            const uint16_t *src = baseB + (min(c0 + row, g.C - 1) - c0) * g.ldb + gp;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gp + 8 <= g.P)
-                v = load16(src);
-            else if (gp < g.P)
-                v = load_partial(src, static_cast<int>(g.P - gp));
-            *reinterpret_cast<uint4 *>(&lB[row * BK + ((ccol ^ lds_swz<BK>(row)) * 8)]) = v;
-        }
-    };
+    OpA opA;
+    OpB opB;
+    if constexpr (AT)
+        opA.init(g.A, g.lda, r0, g.R, g.P, tid);
+    else
+        opA.init(g.A, g.lda, r0, g.R, g.P, wave, lane);
+    if constexpr (BT)
+        opB.init(g.B, g.ldb, c0, g.C, g.P, tid);
+    else
+        opB.init(g.B, g.ldb, c0, g.C, g.P, wave, lane);
 
     // Per-lane fragment addressing.  Fragment i of a wave covers tile rows
     // wr*TR + 32i + (lane%32); the XOR key of its chunk index (lane/32 is the
@@ -537,32 +649,45 @@ gemm_nt_big(GemmProblem g, TileMap tm)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j],
                                                                     acc[i][j], 0, 0, 0);
     };
+    auto compute_stage = [&](const uint16_t *lA, const uint16_t *lB) {
+        frag_load(lA, lB, 1, 1);
+        mfma_rows(0, 0, FR);
+        frag_load(lA, lB, 2, 0);
+        mfma_rows(1, 0, FR);
+        frag_load(lA, lB, 3, 1);
+        mfma_rows(0, 0, FR);
+        mfma_rows(1, 0, FR);
+    };
 
-    // One steady-state stage: compute stage kt from (cA, cB) while stage
-    // kt+1 (wholly inside P) streams straight into (nA, nB).  Fragment reads
-    // run one k step ahead of the MFMAs; the direct loads are spread over the
-    // first k step; the workgroup barrier (after this wave's direct loads have
-    // landed) sits halfway through the last k step so the first fragment
-    // reads of stage kt+1 are covered by the remaining MFMAs.
-    auto stage_dma = [&](const uint16_t *cA, const uint16_t *cB, uint16_t *nA, uint16_t *nB,
-                         int64_t kt) {
-        const int64_t p1 = (kt + 1) * BK;
-#pragma unroll
-        for (int i = 0; i < NBA; ++i)
-            dma_a(nA, p1, i);
-#pragma unroll
-        for (int i = 0; i < NBB; ++i)
-            dma_b(nB, p1, i);
+    // One steady-state stage (see the comment above the kernel).
+    auto stage_fast = [&](const uint16_t *cA, const uint16_t *cB, uint16_t *nA, uint16_t *nB,
+                          int64_t kt) {
+        if constexpr (!AT)
+            opA.dma(nA, (kt + 1) * BK, wave);
+        if constexpr (!BT)
+            opB.dma(nB, (kt + 1) * BK, wave);
         frag_load(cA, cB, 1, 1);
         mfma_rows(0, 0, FR);
         frag_load(cA, cB, 2, 0);
         mfma_rows(1, 0, FR);
         frag_load(cA, cB, 3, 1);
         mfma_rows(0, 0, FR);
+        if constexpr (AT) {
+            opA.store(nA);
+            opA.load_fast((kt + 2) * BK);
+        }
+        if constexpr (BT) {
+            opB.store(nB);
+            opB.load_fast((kt + 2) * BK);
+        }
         mfma_rows(1, 0, FR / 2);
         constexpr int nmf = FR * FC;
         constexpr int nrd = FR + FC;
-        constexpr int ndma = NBA + NBB;
+        constexpr int ndma = (AT ? 0 : OpA::NB) + (BT ? 0 : OpB::NB);
+        constexpr int ntw = OpA::W + OpB::W;                   // LDS writes (transposed)
+        constexpr int ntl = (AT ? 8 : 0) + (BT ? 8 : 0);       // their register loads
+        constexpr int WPM = (ntw + nmf - 1) / nmf;             // per MFMA of k step 2
+        constexpr int LPM = (ntl + nmf - 1) / nmf;
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
 #pragma unroll
@@ -572,6 +697,10 @@ gemm_nt_big(GemmProblem g, TileMap tm)
                 __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
                 if (m < nrd)
                     __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                if (s == 2 && WPM > 0 && m * WPM < ntw)
+                    __builtin_amdgcn_sched_group_barrier(kSgDsWrite, WPM, 0);
+                if (s == 2 && LPM > 0 && m * LPM < ntl)
+                    __builtin_amdgcn_sched_group_barrier(kSgVmemRead, LPM, 0);
             }
         }
         __builtin_amdgcn_sched_group_barrier(kSgMfma, nmf / 2, 0);
@@ -587,43 +716,57 @@ gemm_nt_big(GemmProblem g, TileMap tm)
     const int64_t nk = (g.P + BK - 1) / BK;
     const int64_t nfull = g.P / BK;
     int64_t kt = 0;
+    // Prologue: stage 0 into stage buffer 0; transposed operands also fetch
+    // stage 1 into registers.
     if (nk > 0) {
-        if (nfull > 0) {
-#pragma unroll
-            for (int i = 0; i < NBA; ++i)
-                dma_a(sA0, 0, i);
-#pragma unroll
-            for (int i = 0; i < NBB; ++i)
-                dma_b(sB0, 0, i);
+        const bool fast0 = interior && nfull > 0;
+        const bool fast1 = interior && nfull > 1;
+        if constexpr (AT) {
+            if (fast0) opA.load_fast(0); else opA.load_guarded(0);
+            opA.store(sA0);
+            if (nk > 1) { if (fast1) opA.load_fast(BK); else opA.load_guarded(BK); }
         } else {
-            staged_load(sA0, sB0, 0);
+            if (fast0) opA.dma(sA0, 0, wave); else opA.template staged<NT>(sA0, 0, tid);
+        }
+        if constexpr (BT) {
+            if (fast0) opB.load_fast(0); else opB.load_guarded(0);
+            opB.store(sB0);
+            if (nk > 1) { if (fast1) opB.load_fast(BK); else opB.load_guarded(BK); }
+        } else {
+            if (fast0) opB.dma(sB0, 0, wave); else opB.template staged<NT>(sB0, 0, tid);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         frag_load(sA0, sB0, 0, 0);
     }
-    for (; kt + 2 < nfull; kt += 2) {
-        stage_dma(sA0, sB0, sA1, sB1, kt);
-        stage_dma(sA1, sB1, sA0, sB0, kt + 1);
+    if (interior) {
+        for (; kt + 3 < nfull; kt += 2) {
+            stage_fast(sA0, sB0, sA1, sB1, kt);
+            stage_fast(sA1, sB1, sA0, sB0, kt + 1);
+        }
     }
-    if (kt + 1 < nfull) {
-        stage_dma(sA0, sB0, sA1, sB1, kt);
-        ++kt;
-    }
-    // Drain: the last full stage and the ragged tail (register-staged).
+    // Remaining stages (all of them for an edge tile): guarded loads.  On
+    // entry, stage kt is in stage buffer kt&1 with its first fragments read,
+    // and transposed operands hold stage kt+1 in registers.
     for (; kt < nk; ++kt) {
         uint16_t *cA = (kt & 1) ? sA1 : sA0;
         uint16_t *cB = (kt & 1) ? sB1 : sB0;
         uint16_t *nA = (kt & 1) ? sA0 : sA1;
         uint16_t *nB = (kt & 1) ? sB0 : sB1;
-        frag_load(cA, cB, 1, 1);
-        mfma_rows(0, 0, FR);
-        frag_load(cA, cB, 2, 0);
-        mfma_rows(1, 0, FR);
-        frag_load(cA, cB, 3, 1);
-        mfma_rows(0, 0, FR);
-        mfma_rows(1, 0, FR);
-        if (kt + 1 < nk)
-            staged_load(nA, nB, (kt + 1) * BK);
+        compute_stage(cA, cB);
+        if (kt + 1 < nk) {
+            if constexpr (AT) {
+                opA.store(nA);
+                if (kt + 2 < nk) opA.load_guarded((kt + 2) * BK);
+            } else {
+                opA.template staged<NT>(nA, (kt + 1) * BK, tid);
+            }
+            if constexpr (BT) {
+                opB.store(nB);
+                if (kt + 2 < nk) opB.load_guarded((kt + 2) * BK);
+            } else {
+                opB.template staged<NT>(nB, (kt + 1) * BK, tid);
+            }
+        }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + 1 < nk)
             frag_load(nA, nB, 0, 0);
@@ -661,11 +804,20 @@ gemm_nt_big(GemmProblem g, TileMap tm)
                 } else {
                     float *out = static_cast<float *>(g.D) + c * g.ldd + r;
                     if (full) {
-                        *reinterpret_cast<float4 *>(out) = make_float4(v0, v1, v2, v3);
+                        float4 w = make_float4(v0, v1, v2, v3);
+                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
+                            const float4 o = *reinterpret_cast<const float4 *>(out);
+                            w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
+                        }
+                        *reinterpret_cast<float4 *>(out) = w;
                     } else {
                         const float vv[4] = {v0, v1, v2, v3};
-                        for (int e = 0; e < 4 && r + e < g.R; ++e)
-                            out[e] = vv[e];
+                        for (int e = 0; e < 4 && r + e < g.R; ++e) {
+                            if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
+                                out[e] = out[e] + vv[e];
+                            else
+                                out[e] = vv[e];
+                        }
                     }
                 }
             }
@@ -673,7 +825,7 @@ gemm_nt_big(GemmProblem g, TileMap tm)
     }
 }
 
-template <int BR, int BC, int WR, int WC>
+template <int BR, int BC, int WR, int WC, bool AT, bool BT>
 hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
     constexpr int BK = 64;
@@ -685,10 +837,17 @@ hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     if (nwg == 0)
         return hipSuccess;
     dim3 grid(static_cast<unsigned>(nwg)), block(WR * WC * 64);
-    if (epi == Epi::kStoreBF16)
-        hipLaunchKernelGGL((gemm_nt_big<BR, BC, BK, WR, WC, 1>), grid, block, 0, s, p, tm);
-    else
-        hipLaunchKernelGGL((gemm_nt_big<BR, BC, BK, WR, WC, 0>), grid, block, 0, s, p, tm);
+    switch (epi) {
+    case Epi::kStoreF32:
+        hipLaunchKernelGGL((gemm_big<BR, BC, BK, WR, WC, AT, BT, 0>), grid, block, 0, s, p, tm);
+        break;
+    case Epi::kStoreBF16:
+        hipLaunchKernelGGL((gemm_big<BR, BC, BK, WR, WC, AT, BT, 1>), grid, block, 0, s, p, tm);
+        break;
+    case Epi::kAccumF32:
+        hipLaunchKernelGGL((gemm_big<BR, BC, BK, WR, WC, AT, BT, 2>), grid, block, 0, s, p, tm);
+        break;
+    }
     return hipGetLastError();
 }
 
@@ -720,28 +879,53 @@ hipError_t launch_cfg(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 
 }  // namespace
 
+// The large-tile kernel addresses a tile through 32-bit byte offsets: its
+// span must stay below 2^31 bytes (256 rows of the operand plus one stage).
+static bool big_offsets_fit(const GemmProblem &p)
+{
+    return (256 * std::max(p.lda, p.ldb) + 64) * 2 < (int64_t(1) << 31) &&
+           (64 * std::max(p.lda, p.ldb) + 256) * 2 < (int64_t(1) << 31);
+}
+
 hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 {
-    // R = V (vocabulary), C = M (tokens).  The large-tile kernel addresses a
-    // tile through 32-bit byte offsets: keep its span below 2^31 bytes.
-    const bool offsets_fit = (256 * std::max(p.lda, p.ldb) + 64) * 2 < (int64_t(1) << 31);
-    if (!offsets_fit)
+    // R = V (vocabulary), C = M (tokens); both operands K-contiguous.
+    if (!big_offsets_fit(p))
         return launch_cfg<128, 128, 2, 2, false, false>(p, epi, 8, s);
     if (p.C <= 128)
-        return launch_big<128, 128, 2, 2>(p, epi, 8, s);
-    return launch_big<256, 256, 4, 2>(p, epi, 8, s);
+        return launch_big<128, 128, 2, 2, false, false>(p, epi, 8, s);
+    return launch_big<256, 256, 4, 2, false, false>(p, epi, 8, s);
+}
+
+// dgrad / wgrad tile choice (measured on MI355X at M=1024 K=8192 V=32768 and
+// M=4096 K=16384 V=131072): 256x256 tiles with 4 waves (128x128 accumulators
+// per wave, room for two transposed staging sets) whenever there are enough
+// tiles to fill the chip; otherwise dgrad's short output (M x K) is split
+// into 256x128 tiles with 8 waves, and tiny problems use 128x128.
+template <bool AT, bool BT>
+hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
+{
+    if (!big_offsets_fit(p))
+        return launch_cfg<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
+    const int64_t tiles256 = ((p.R + 255) / 256) * ((p.C + 255) / 256);
+    const int64_t tiles256x128 = ((p.R + 255) / 256) * ((p.C + 127) / 128);
+    if (tiles256 >= 512 || (BT && tiles256 >= 256))
+        return launch_big<256, 256, 2, 2, AT, BT>(p, epi, 8, s);
+    if (tiles256x128 >= 192)
+        return launch_big<256, 128, 4, 2, AT, BT>(p, epi, 8, s);
+    return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
 }
 
 hipError_t launch_gemm_dgrad(const GemmProblem &p, Epi epi, hipStream_t s)
 {
-    // R = K (hidden), C = M (tokens), A = W stored [V][K] (transposed).
-    return launch_cfg<128, 128, 2, 2, true, false>(p, epi, 8, s);
+    // R = K (hidden), C = M (tokens), A = W stored [V][K] (p-major).
+    return launch_bwd<true, false>(p, epi, s);
 }
 
 hipError_t launch_gemm_wgrad(const GemmProblem &p, Epi epi, hipStream_t s)
 {
     // R = K (hidden), C = V (vocabulary); both operands stored [M][*].
-    return launch_cfg<128, 128, 2, 2, true, true>(p, epi, 8, s);
+    return launch_bwd<true, true>(p, epi, s);
 }
 
 }  // namespace lmh

@@ -205,3 +205,47 @@ def test_wgrad_random_sampled():
     rows = np.array([0, 5, 4095, 4096, 20000, 32767])
     ref, S = oracle.wgrad(dl_bits, x_bits, rows=rows)
     assert_gemm_close(host_f32(dw)[rows], ref, S, 1e-5, "wgrad")
+
+
+# ------------------------------------------- steady-state paths, integer exact
+
+def test_logits_integer_exact_interior_tiles():
+    """M=512 K=1024 V=2048: 256x256 8-wave tiles, all interior, 16 full
+    stages (the direct-to-LDS steady loop) -- bit-exact FP32 and BF16."""
+    inp = workloads.integer_gemm(512, 1024, 2048, seed=31, with_targets=False)
+    _say("logits int interior 512x1024x2048")
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    out = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    outb = lmh.lmhead_logits(x, W, out_dtype="bf16")
+    torch.cuda.synchronize()
+    L, _ = oracle.logits(inp.x, inp.W)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(L.astype(np.float32)))
+    assert np.array_equal(host_bits(outb), oracle.round_bf16(L))
+
+
+def test_dgrad_integer_exact_interior_tiles():
+    """M=1024 K=8192 V=4096: dgrad runs 256x128 8-wave tiles with the
+    register-transposed W operand; sampled rows bit-exact."""
+    dl_bits, W_bits = workloads.integer_operands([(1024, 4096), (4096, 8192)], seed=41)
+    _say("dgrad int interior 1024x8192x4096")
+    dX = lmh.lmhead_dgrad(dev_bf16(dl_bits), dev_bf16(W_bits), dx_dtype="fp32")
+    torch.cuda.synchronize()
+    rows = np.array([0, 3, 255, 256, 700, 1023])
+    ref, _ = oracle.dgrad(dl_bits, W_bits, rows=rows)
+    assert np.array_equal(_f32_bits(host_f32(dX)[rows]), _f32_bits(ref.astype(np.float32)))
+
+
+def test_wgrad_integer_exact_interior_tiles():
+    """M=2048 K=4096 V=8192: wgrad runs 256x256 4-wave tiles with both
+    operands register-transposed; sampled rows bit-exact, then accumulate."""
+    dl_bits, x_bits = workloads.integer_operands([(2048, 8192), (2048, 4096)], seed=43)
+    _say("wgrad int interior 2048x4096x8192")
+    dl, x = dev_bf16(dl_bits), dev_bf16(x_bits)
+    dW = lmh.lmhead_wgrad(dl, x)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 4097, 8191])
+    ref, _ = oracle.wgrad(dl_bits, x_bits, rows=rows)
+    assert np.array_equal(_f32_bits(host_f32(dW)[rows]), _f32_bits(ref.astype(np.float32)))
+    lmh.lmhead_wgrad(dl, x, dW=dW, accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_f32_bits(host_f32(dW)[rows]), _f32_bits((2 * ref).astype(np.float32)))
