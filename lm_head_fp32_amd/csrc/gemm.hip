@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace lmh {
 namespace {
@@ -545,6 +546,65 @@ struct TransOperand {
     }
 };
 
+// Epilogue shared by the large-tile kernels: lane l, register 4q+e of a
+// 32x32 accumulator tile holds row 8q + 4(l/32) + e, column l%32, so four
+// consecutive R values per lane go out as one 16-byte (FP32) or 8-byte
+// (BF16) store; rows and columns past the edge are not stored.
+template <int FR, int FC, int EPI>
+__device__ __forceinline__ void store_tile(const GemmProblem &g, f32x16 (&acc)[FR][FC],
+                                           int64_t rbase, int64_t cbase, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+#pragma unroll
+        for (int j = 0; j < FC; ++j) {
+            const int64_t c = cbase + j * 32 + (lane & 31);
+            if (c >= g.C)
+                continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = rbase + i * 32 + q * 8 + (lane >> 5) * 4;
+                if (r >= g.R)
+                    continue;
+                const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                const bool full = r + 4 <= g.R;
+                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
+                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
+                    if (full) {
+                        uint2 w;
+                        w.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+                        w.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+                        *reinterpret_cast<uint2 *>(out) = w;
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e)
+                            out[e] = static_cast<uint16_t>(f32_to_bf16_bits(vv[e]));
+                    }
+                } else {
+                    float *out = static_cast<float *>(g.D) + c * g.ldd + r;
+                    if (full) {
+                        float4 w = make_float4(v0, v1, v2, v3);
+                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
+                            const float4 o = *reinterpret_cast<const float4 *>(out);
+                            w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
+                        }
+                        *reinterpret_cast<float4 *>(out) = w;
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e) {
+                            if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
+                                out[e] = out[e] + vv[e];
+                            else
+                                out[e] = vv[e];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gemm_big: BR x BC tiles, WR x WC waves (two per SIMD with 8 waves), BK = 64.
 // Operands whose contraction dimension is contiguous stream into LDS by
@@ -593,7 +653,9 @@ gemm_big(GemmProblem g, TileMap tm)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int wr = wave % WR;
     const int wc = wave / WR;
-    const bool interior = (r0 + BR <= g.R) && (c0 + BC <= g.C);
+    // Direct-load operands clamp rows past the edge (those outputs are never
+    // stored); only transposed operands need the tile inside the rows.
+    const bool interior = (!AT || r0 + BR <= g.R) && (!BT || c0 + BC <= g.C);
 
     OpA opA;
     OpB opB;
@@ -772,57 +834,171 @@ gemm_big(GemmProblem g, TileMap tm)
             frag_load(nA, nB, 0, 0);
     }
 
-    // Epilogue: lane l, register 4q+e of a 32x32 tile = row 8q + 4(l/32) + e,
-    // column l%32; four consecutive R values per lane -> one 16-byte store.
+    store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + wc * TC, lane);
+}
+
+// ---------------------------------------------------------------------------
+// gemm_small: the logits GEMM for few tokens (M <= 256), where the work is
+// bound by streaming W once from HBM.  Tiles of 128 vocabulary rows x BC
+// tokens (BC = 32, 64 or 128), 4 waves (each 32 rows x BC), BK = 64, and a
+// ring of S LDS stages filled by direct buffer loads: S-1 stages are in
+// flight while one is consumed, which keeps enough bytes moving per CU to
+// approach the HBM rate.  The steady loop is unrolled S times so that every
+// stage buffer is a compile-time choice (the compiler then knows the loads
+// in flight never touch the buffer being read).
+template <int... I, typename F>
+__device__ __forceinline__ void unroll_seq(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// One LDS array per (TAG, size): distinct variables let the compiler prove
+// that a direct load into one ring stage never touches another.
+template <int TAG, int N>
+__device__ __forceinline__ uint16_t *lds_array()
+{
+    __shared__ __attribute__((aligned(16))) uint16_t buf[N];
+    return buf;
+}
+
+template <int BC, int S, int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_small(GemmProblem g, TileMap tm)
+{
+    constexpr int BR = 128, BK = 64, NW = 4;
+    constexpr int FR = 1, FC = BC / 32;
+    using OpA = DmaOperand<BR, BK, NW>;
+    using OpB = DmaOperand<BC, BK, NW>;
+    constexpr int NBW = OpA::NB + OpB::NB;  // direct loads per wave per stage
+    static_assert(S >= 3, "ring of at least three stages");
+
+    // Stage buffers: sA(b) / sB(b) for a compile-time b, and tables for the
+    // runtime-indexed tail.
+    auto sA_c = [](auto bc) { return lds_array<2 * decltype(bc)::value, BR * BK>(); };
+    auto sB_c = [](auto bc) { return lds_array<2 * decltype(bc)::value + 1, BC * BK>(); };
+    uint16_t *sA[S];
+    uint16_t *sB[S];
+    unroll_seq(std::make_integer_sequence<int, S>{}, [&](auto bc) {
+        sA[decltype(bc)::value] = sA_c(bc);
+        sB[decltype(bc)::value] = sB_c(bc);
+    });
+
+    int tr, tc;
+    map_tile(tm, tr, tc);
+    const int64_t r0 = static_cast<int64_t>(tr) * BR;
+    const int64_t c0 = static_cast<int64_t>(tc) * BC;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    OpA opA;
+    OpB opB;
+    opA.init(g.A, g.lda, r0, g.R, g.P, wave, lane);
+    opB.init(g.B, g.ldb, c0, g.C, g.P, wave, lane);
+
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    const int fbA = (wave * 32 + lrow) * BK;
+    const int fbB = lrow * BK;
+    const int keyA = khalf ^ lds_swz<BK>(wave * 32 + lrow);
+    int keyB[2];
 #pragma unroll
-    for (int i = 0; i < FR; ++i) {
+    for (int par = 0; par < 2; ++par)
+        keyB[par] = khalf ^ lds_swz<BK>(par * 32 + lrow);
+
+    f32x16 acc[FR][FC];
 #pragma unroll
-        for (int j = 0; j < FC; ++j) {
-            const int64_t c = c0 + wc * TC + j * 32 + (lane & 31);
-            if (c >= g.C)
-                continue;
+    for (int j = 0; j < FC; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t r = r0 + wr * TR + i * 32 + q * 8 + (lane >> 5) * 4;
-                if (r >= g.R)
-                    continue;
-                const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                const bool full = r + 4 <= g.R;
-                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
-                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
-                    if (full) {
-                        uint2 w;
-                        w.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-                        w.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-                        *reinterpret_cast<uint2 *>(out) = w;
-                    } else {
-                        const float vv[4] = {v0, v1, v2, v3};
-                        for (int e = 0; e < 4 && r + e < g.R; ++e)
-                            out[e] = static_cast<uint16_t>(f32_to_bf16_bits(vv[e]));
-                    }
-                } else {
-                    float *out = static_cast<float *>(g.D) + c * g.ldd + r;
-                    if (full) {
-                        float4 w = make_float4(v0, v1, v2, v3);
-                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
-                            const float4 o = *reinterpret_cast<const float4 *>(out);
-                            w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
-                        }
-                        *reinterpret_cast<float4 *>(out) = w;
-                    } else {
-                        const float vv[4] = {v0, v1, v2, v3};
-                        for (int e = 0; e < 4 && r + e < g.R; ++e) {
-                            if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
-                                out[e] = out[e] + vv[e];
-                            else
-                                out[e] = vv[e];
-                        }
-                    }
-                }
-            }
+        for (int e = 0; e < 16; ++e)
+            acc[0][j][e] = 0.0f;
+
+    auto compute = [&](const uint16_t *lA, const uint16_t *lB) {
+        bf16x8 fa[2], fb[2][FC];
+        auto fl = [&](int kk, int slot) {
+            fa[slot] = *reinterpret_cast<const bf16x8 *>(&lA[fbA + (((2 * kk) ^ keyA) * 8)]);
+            const int kb0 = ((2 * kk) ^ keyB[0]) * 8, kb1 = ((2 * kk) ^ keyB[1]) * 8;
+#pragma unroll
+            for (int j = 0; j < FC; ++j)
+                fb[slot][j] = *reinterpret_cast<const bf16x8 *>(
+                    &lB[fbB + j * 32 * BK + ((j & 1) ? kb1 : kb0)]);
+        };
+        fl(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4)
+                fl(kk + 1, (kk + 1) & 1);
+#pragma unroll
+            for (int j = 0; j < FC; ++j)
+                acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1], fb[kk & 1][j],
+                                                                    acc[0][j], 0, 0, 0);
         }
+    };
+
+    const int64_t nk = (g.P + BK - 1) / BK;
+    const int64_t nfull = g.P / BK;
+    // Prologue: the first S-1 full stages go in flight.
+    unroll_seq(std::make_integer_sequence<int, S - 1>{}, [&](auto bc) {
+        constexpr int st = decltype(bc)::value;
+        if (st < nfull) {
+            opA.dma(sA_c(bc), static_cast<int64_t>(st) * BK, wave);
+            opB.dma(sB_c(bc), static_cast<int64_t>(st) * BK, wave);
+        }
+    });
+    int64_t kt = 0;
+    // Steady state: S consecutive stages per trip, each waiting only for its
+    // own loads (the S-2 later stages stay in flight), then refilling the
+    // buffer freed by the previous stage.
+    for (; kt + 2 * S - 2 < nfull; kt += S) {
+        unroll_seq(std::make_integer_sequence<int, S>{}, [&](auto bc) {
+            constexpr int b = decltype(bc)::value;
+            constexpr int bn = (b + S - 1) % S;
+            constexpr int outstanding = (S - 2) * NBW;
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(outstanding) : "memory");
+            const int64_t pn = (kt + b + S - 1) * BK;
+            const std::integral_constant<int, bn> bnc;
+            opA.dma(sA_c(bnc), pn, wave);
+            opB.dma(sB_c(bnc), pn, wave);
+            compute(sA_c(bc), sB_c(bc));
+        });
     }
+    // Remaining stages: conservative waits; a ragged last stage is loaded
+    // through registers with zero fill past P.
+    for (; kt < nk; ++kt) {
+        const int b = static_cast<int>(kt % S);
+        if (kt >= nfull) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            opA.template staged<256>(sA[b], kt * BK, tid);
+            opB.template staged<256>(sB[b], kt * BK, tid);
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kt + S - 1 < nfull) {
+            const int bn = static_cast<int>((kt + S - 1) % S);
+            opA.dma(sA[bn], (kt + S - 1) * BK, wave);
+            opB.dma(sB[bn], (kt + S - 1) * BK, wave);
+        }
+        compute(sA[b], sB[b]);
+    }
+    store_tile<FR, FC, EPI>(g, acc, r0 + wave * 32, c0, lane);
+}
+
+template <int BC, int S>
+hipError_t launch_small(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
+{
+    TileMap tm;
+    tm.tiles_r = static_cast<int>((p.R + 127) / 128);
+    tm.tiles_c = static_cast<int>((p.C + BC - 1) / BC);
+    tm.group_r = group_r < 1 ? 1 : group_r;
+    const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
+    if (nwg == 0)
+        return hipSuccess;
+    if (epi == Epi::kStoreBF16)
+        hipLaunchKernelGGL((gemm_small<BC, S, 1>), dim3(static_cast<unsigned>(nwg)), dim3(256), 0,
+                           s, p, tm);
+    else
+        hipLaunchKernelGGL((gemm_small<BC, S, 0>), dim3(static_cast<unsigned>(nwg)), dim3(256), 0,
+                           s, p, tm);
+    return hipGetLastError();
 }
 
 template <int BR, int BC, int WR, int WC, bool AT, bool BT>
@@ -887,13 +1063,35 @@ static bool big_offsets_fit(const GemmProblem &p)
            (64 * std::max(p.lda, p.ldb) + 256) * 2 < (int64_t(1) << 31);
 }
 
+#ifndef LMH_SMALLM_CFG
+#define LMH_SMALLM_CFG 0
+#endif
+
 hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 {
     // R = V (vocabulary), C = M (tokens); both operands K-contiguous.
     if (!big_offsets_fit(p))
         return launch_cfg<128, 128, 2, 2, false, false>(p, epi, 8, s);
-    if (p.C <= 128)
-        return launch_big<128, 128, 2, 2, false, false>(p, epi, 8, s);
+    switch (LMH_SMALLM_CFG) {  // pinned shapes for tuning builds
+    case 1: return launch_big<128, 128, 2, 2, false, false>(p, epi, 8, s);
+    case 2: return launch_small<128, 4>(p, epi, 8, s);
+    case 3: return launch_small<64, 6>(p, epi, 8, s);
+    case 4: return launch_small<32, 6>(p, epi, 8, s);
+    case 5: return launch_big<256, 256, 4, 2, false, false>(p, epi, 8, s);
+    default: break;
+    }
+#ifndef LMH_SMALL_S32
+#define LMH_SMALL_S32 8
+#endif
+#ifndef LMH_SMALL_S128
+#define LMH_SMALL_S128 5
+#endif
+    if (p.C <= 32)
+        return launch_small<32, LMH_SMALL_S32>(p, epi, 8, s);
+    if (p.C <= 64)
+        return launch_small<64, 6>(p, epi, 8, s);
+    if (p.C <= 256)
+        return launch_small<128, LMH_SMALL_S128>(p, epi, 8, s);
     return launch_big<256, 256, 4, 2, false, false>(p, epi, 8, s);
 }
 
