@@ -26,6 +26,42 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load / store of four FP32 values, optionally marked non-temporal
+// (streamed once: do not keep the lines in the caches).
+template <bool NT>
+__device__ __forceinline__ float4 ld4(const float4 *p)
+{
+    if constexpr (NT) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+template <bool NT>
+__device__ __forceinline__ void st4(float4 *p, const float4 &v)
+{
+    if constexpr (NT) {
+        const f32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p));
+    } else {
+        *p = v;
+    }
+}
+template <bool NT>
+__device__ __forceinline__ void st2u(uint2 *p, const uint2 &v)
+{
+    if constexpr (NT) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = {v.x, v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
+    } else {
+        *p = v;
+    }
+}
+
 __device__ __forceinline__ float exp_shifted(float z, float m)
 {
     return __builtin_amdgcn_exp2f((z - m) * kLog2e);
@@ -48,7 +84,7 @@ __device__ __forceinline__ float max4(const float4 &v)
     return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
 }
 
-template <int NT, int U>
+template <int NT, int U, bool NTL>
 __global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ z, int64_t ld,
                                                       int64_t V, const int32_t *__restrict__ tgt,
                                                       int32_t ignore_index, float *__restrict__ loss,
@@ -68,7 +104,8 @@ __global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = base + u * NT + tid;
-            v[u] = (i < n4) ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            v[u] = (i < n4) ? ld4<NTL>(z4 + i)
+                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
         float bm = max4(v[0]);
 #pragma unroll
@@ -136,7 +173,7 @@ __global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ 
 
 // Gradient of one row chunk.  OUTBF16 selects the store type only; the FP32
 // value is computed identically in both instantiations.
-template <int NT, int U, bool OUTBF16>
+template <int NT, int U, bool OUTBF16, bool NTL, bool NTS>
 __global__ __launch_bounds__(NT) void xent_bwd_kernel(const float *z, int64_t ld,
                                                       const float4 *__restrict__ stats,
                                                       const int32_t *__restrict__ tgt,
@@ -169,7 +206,7 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(const float *z, int64_t ld
         for (int u = 0; u < U; ++u) {
             const int64_t i = first + u * NT + tid;
             if (i < n4)
-                v[u] = z4[i];
+                v[u] = ld4<NTL>(z4 + i);
         }
     }
 #pragma unroll
@@ -181,28 +218,26 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(const float *z, int64_t ld
         if (ignored) {
             o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         } else {
-            o.x = exp_shifted(v[u].x, m) * coef;
-            o.y = exp_shifted(v[u].y, m) * coef;
-            o.z = exp_shifted(v[u].z, m) * coef;
-            o.w = exp_shifted(v[u].w, m) * coef;
-            const int64_t j0 = 4 * i;
-            if (static_cast<int64_t>(y) >= j0 && static_cast<int64_t>(y) < j0 + 4) {
-                const int e = static_cast<int>(y - j0);
-                const float vy = e == 0 ? v[u].x : e == 1 ? v[u].y : e == 2 ? v[u].z : v[u].w;
-                const float gy = fmaf(exp_shifted(vy, m), coef, -up);
-                if (e == 0) o.x = gy;
-                else if (e == 1) o.y = gy;
-                else if (e == 2) o.z = gy;
-                else o.w = gy;
-            }
+            // Each lane picks its own value with a select; the target column
+            // gets the one-hot term folded in by a single fused multiply-add.
+            // Written without branches on purpose: a branching form that wrote
+            // one of four lanes was compiled into code that placed the target
+            // term in the wrong lane at one unroll factor.
+            const int64_t e = static_cast<int64_t>(y) - 4 * i;
+            const float ex = exp_shifted(v[u].x, m), ey = exp_shifted(v[u].y, m);
+            const float ez = exp_shifted(v[u].z, m), ew = exp_shifted(v[u].w, m);
+            o.x = (e == 0) ? fmaf(ex, coef, -up) : ex * coef;
+            o.y = (e == 1) ? fmaf(ey, coef, -up) : ey * coef;
+            o.z = (e == 2) ? fmaf(ez, coef, -up) : ez * coef;
+            o.w = (e == 3) ? fmaf(ew, coef, -up) : ew * coef;
         }
         if constexpr (OUTBF16) {
             uint2 w;
             w.x = f32_to_bf16_bits(o.x) | (f32_to_bf16_bits(o.y) << 16);
             w.y = f32_to_bf16_bits(o.z) | (f32_to_bf16_bits(o.w) << 16);
-            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g) + row * ldg)[i] = w;
+            st2u<NTS>(reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g) + row * ldg) + i, w);
         } else {
-            reinterpret_cast<float4 *>(static_cast<float *>(g) + row * ldg)[i] = o;
+            st4<NTS>(reinterpret_cast<float4 *>(static_cast<float *>(g) + row * ldg) + i, o);
         }
     }
     // Tail: last V % 4 columns, handled by the row's last chunk.
@@ -262,6 +297,31 @@ __global__ __launch_bounds__(kMeanThreads) void xent_mean_kernel(const float *__
 
 }  // namespace
 
+// Launch shapes, chosen by timing on 8192 x 131072 FP32 logits (overridable at
+// build time for sweeps).  Both kernels stream every byte once, so the loads of
+// the forward pass and the loads and stores of the backward pass are marked
+// non-temporal.  Forward: one 256-thread block per row, four 16-byte loads in
+// flight per thread.  Backward: 128-thread blocks, each owning 2 x 128 float4
+// of one row, which keeps enough small blocks resident to cover HBM latency.
+#ifndef LMH_XF_U
+#define LMH_XF_U 4
+#endif
+#ifndef LMH_XF_NTL
+#define LMH_XF_NTL true
+#endif
+#ifndef LMH_XB_NT
+#define LMH_XB_NT 128
+#endif
+#ifndef LMH_XB_U
+#define LMH_XB_U 2
+#endif
+#ifndef LMH_XB_NTL
+#define LMH_XB_NTL true
+#endif
+#ifndef LMH_XB_NTS
+#define LMH_XB_NTS true
+#endif
+
 hipError_t launch_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
                            const int32_t *target, int32_t ignore_index, float *loss, float *stats,
                            hipStream_t s)
@@ -270,11 +330,13 @@ hipError_t launch_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int6
         return hipSuccess;
     float4 *st = reinterpret_cast<float4 *>(stats);
     if (n_rows < 512) {
-        hipLaunchKernelGGL((xent_fwd_kernel<1024, 4>), dim3(static_cast<unsigned>(n_rows)),
-                           dim3(1024), 0, s, logits, ld, n_cols, target, ignore_index, loss, st);
+        hipLaunchKernelGGL((xent_fwd_kernel<1024, 4, LMH_XF_NTL>),
+                           dim3(static_cast<unsigned>(n_rows)), dim3(1024), 0, s, logits, ld, n_cols,
+                           target, ignore_index, loss, st);
     } else {
-        hipLaunchKernelGGL((xent_fwd_kernel<256, 4>), dim3(static_cast<unsigned>(n_rows)),
-                           dim3(256), 0, s, logits, ld, n_cols, target, ignore_index, loss, st);
+        hipLaunchKernelGGL((xent_fwd_kernel<256, LMH_XF_U, LMH_XF_NTL>),
+                           dim3(static_cast<unsigned>(n_rows)), dim3(256), 0, s, logits, ld, n_cols,
+                           target, ignore_index, loss, st);
     }
     return hipGetLastError();
 }
@@ -294,7 +356,7 @@ hipError_t launch_xent_bwd(const float *logits, int64_t ld, const float *stats,
 {
     if (n_rows == 0)
         return hipSuccess;
-    constexpr int NT = 256, U = 4;
+    constexpr int NT = LMH_XB_NT, U = LMH_XB_U;
     const int64_t n4 = n_cols >> 2;
     int64_t bpr = (n4 + NT * U - 1) / (NT * U);
     if (bpr < 1)
@@ -302,13 +364,13 @@ hipError_t launch_xent_bwd(const float *logits, int64_t ld, const float *stats,
     const int64_t nblk = bpr * n_rows;
     const float4 *st = reinterpret_cast<const float4 *>(stats);
     if (bf16_out)
-        hipLaunchKernelGGL((xent_bwd_kernel<NT, U, true>), dim3(static_cast<unsigned>(nblk)),
-                           dim3(NT), 0, s, logits, ld, st, target, ignore_index, dloss,
-                           dloss_stride, dlogits, ldg, n_cols, bpr);
+        hipLaunchKernelGGL((xent_bwd_kernel<NT, U, true, LMH_XB_NTL, LMH_XB_NTS>),
+                           dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s, logits, ld, st, target,
+                           ignore_index, dloss, dloss_stride, dlogits, ldg, n_cols, bpr);
     else
-        hipLaunchKernelGGL((xent_bwd_kernel<NT, U, false>), dim3(static_cast<unsigned>(nblk)),
-                           dim3(NT), 0, s, logits, ld, st, target, ignore_index, dloss,
-                           dloss_stride, dlogits, ldg, n_cols, bpr);
+        hipLaunchKernelGGL((xent_bwd_kernel<NT, U, false, LMH_XB_NTL, LMH_XB_NTS>),
+                           dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s, logits, ld, st, target,
+                           ignore_index, dloss, dloss_stride, dlogits, ldg, n_cols, bpr);
     return hipGetLastError();
 }
 

@@ -181,6 +181,35 @@ def test_edge_shapes_random(n, V, dloss_mode):
     assert np.all(rs <= 1e-5 * scale + 1e-7)
 
 
+def test_target_lane_every_residue():
+    """The one-hot term lands on the target column whatever its position in
+    its 16-byte group (target mod 4 = 0..3), in the first, middle and last
+    block of a row and in the ragged tail.  With dloss > 0 the target column
+    is the only negative entry of its gradient row (softmax minus one-hot,
+    scaled), so its position is checked exactly, then every value against
+    the oracle."""
+    V = 9 * 1024 + 3
+    cols = [0, 1, 2, 3, 1020, 1021, 1022, 1023, 4100, 4101, 4102, 4103,
+            V - 7, V - 6, V - 5, V - 4, V - 3, V - 2, V - 1]
+    n = len(cols) * 2
+    tgt = np.array(cols + cols, dtype=np.int32)
+    rng = np.random.default_rng(4242)
+    logits = rng.normal(0.0, 1.5, (n, V)).astype(np.float32)
+    dl_host = rng.uniform(0.25, 2.0, n).astype(np.float32)
+    _say(f"target lanes n={n} V={V}")
+    z, t = dev_f32(logits, (V + 3) // 4 * 4), dev_i32(tgt)
+    _, st = lmh.lmhead_xent_fwd(z, t)
+    g = lmh.lmhead_xent_bwd(z, st, t, torch.from_numpy(dl_host).cuda())
+    gb = lmh.lmhead_xent_bwd(z, st, t, torch.from_numpy(dl_host).cuda(), grad_dtype="bf16")
+    torch.cuda.synchronize()
+    gh = host_f32(g)
+    neg = [np.flatnonzero(gh[r] < 0).tolist() for r in range(n)]
+    assert neg == [[int(y)] for y in tgt]
+    g_ref = oracle.xent_bwd(logits, tgt, -100, dl_host.astype(np.float64))
+    _check_grad(gh, g_ref)
+    assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
+
+
 def test_all_rows_ignored_and_bad_target():
     V = 100
     z = dev_f32(np.random.default_rng(1).normal(0, 1, (6, V)).astype(np.float32))
