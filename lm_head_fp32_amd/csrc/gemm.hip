@@ -1001,6 +1001,228 @@ hipError_t launch_small(const GemmProblem &p, Epi epi, int group_r, hipStream_t 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// gemm_pp: the logits GEMM for many tokens (both operands K-contiguous,
+// K a multiple of 32).  256 x 256 tiles, 8 waves of 64 x 128 accumulators,
+// K consumed in stages of 32 held in a ring of four LDS slots that direct
+// buffer loads fill three stages ahead.
+//
+// The waves form two groups (waves 0-3 and 4-7, one of each per SIMD) that
+// run the same sequence, one phase apart ("ping-pong"):
+//   M(s): issue this wave's direct loads of stage s+3, read its stage-s
+//         fragments (two 16-wide k steps) into registers, wait for its loads
+//         of stage s+1; barrier;
+//   C(s): the 16 MFMAs of stage s from registers; barrier.
+// Group 1 enters with one extra barrier, so while one group issues its 16
+// back-to-back MFMAs the other group on the same SIMD does its memory work
+// and waits; the matrix pipe changes hands at every barrier instead of
+// idling through the waits.  Every wave executes 2N + 2 barriers (N stages).
+// Ring safety, with barriers numbered per group: stage s+3 overwrites the
+// slot of stage s-1, whose reads both groups finished (lgkmcnt(0)) before
+// barriers that precede either group's M(s); each wave waits for its own
+// loads of stage s+1 before the barrier that ends its M(s), and both groups'
+// waits precede the barrier after which group 0 runs M(s+1).
+//
+// LDS slot layout per operand: [256 rows][32] BF16 (64-byte rows); the four
+// 16-byte chunks of a row are permuted by pp_swz(row), which keeps both the
+// 1 KiB direct-load blocks and the MFMA fragment reads free of bank
+// conflicts whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int pp_swz(int row)
+{
+    return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+}
+
+// Wait until at most N of this wave's direct loads are in flight.  Inline
+// assembly, like the loads themselves: the compiler neither sees nor adds to
+// the waits of the ring.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LMH_LDS_PTR(p)));
+}
+
+// One 16-byte-per-lane direct load into LDS at lds + 16 * lane, issued from
+// inline assembly so that the compiler does not track it: the kernel's own
+// vmcnt waits and barriers order every use of the destination.  M0 holds the
+// LDS base (an input operand, so the compiler writes it); one wait state
+// separates that write from the load.
+__device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t rs, uint32_t lds,
+                                                uint32_t voff, int soff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+
+__device__ __forceinline__ void pp_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_pp(GemmProblem g, TileMap tm)
+{
+    constexpr int BR = 256, BC = 256, BK = 32, S = 4;
+    constexpr int WR = 4, TR = 64, TC = 128, FR = TR / 32, FC = TC / 32;
+    constexpr int SLOT = 256 * BK;  // BF16 elements per operand per slot (16 KiB)
+    // One LDS array per slot (A then B): the compiler tracks only a few
+    // direct-load targets; beyond that it waits for every load in flight.
+    constexpr int TAG = 64;
+    auto sA = [](auto bc) { return lds_array<TAG + decltype(bc)::value, 2 * SLOT>(); };
+    auto sB = [](auto bc) { return lds_array<TAG + decltype(bc)::value, 2 * SLOT>() + SLOT; };
+
+    int tr, tc;
+    map_tile(tm, tr, tc);
+    const int64_t r0 = static_cast<int64_t>(tr) * BR;
+    const int64_t c0 = static_cast<int64_t>(tc) * BC;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % WR;
+    const int grp = wave / WR;  // also the tile's column half
+
+    // Direct loads: this wave moves rows [32 wave, 32 wave + 32) of both
+    // operand tiles, as two 1 KiB blocks of 16 rows; lane l lands at byte 16 l
+    // of its block (row l/4, slot l%4) and fetches chunk (l%4) ^ pp_swz(row).
+    // Rows past the edge re-read the last valid row (never stored).
+    const __amdgpu_buffer_rsrc_t rsA = tile_rsrc(g.A + r0 * g.lda);
+    const __amdgpu_buffer_rsrc_t rsB = tile_rsrc(g.B + c0 * g.ldb);
+    uint32_t offA[2], offB[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int row = 32 * wave + 16 * b + lane / 4;
+        const int ch = (lane & 3) ^ pp_swz(row);
+        offA[b] = static_cast<uint32_t>(((min(r0 + row, g.R - 1) - r0) * g.lda + ch * 8) * 2);
+        offB[b] = static_cast<uint32_t>(((min(c0 + row, g.C - 1) - c0) * g.ldb + ch * 8) * 2);
+    }
+    auto dma = [&](uint16_t *lA, uint16_t *lB, int64_t st) {
+        const int soff = static_cast<int>(st * BK * 2);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            dma16_untracked(rsA, lds_addr(lA + (2 * wave + b) * 512), offA[b], soff);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            dma16_untracked(rsB, lds_addr(lB + (2 * wave + b) * 512), offB[b], soff);
+    };
+
+    // Fragment reads: fragment i of the wave covers tile rows wr*TR + 32i +
+    // lane%32; pp_swz of those rows depends on lane%32 only.
+    const int key = pp_swz(lane & 31);
+    const int hk = lane >> 5;
+    const int fbA = (wr * TR + (lane & 31)) * BK;
+    const int fbB = (grp * TC + (lane & 31)) * BK;
+    bf16x8 fa[2][FR], fb[2][FC];
+    auto frag_read = [&](const uint16_t *lA, const uint16_t *lB) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ch = ((2 * kk + hk) ^ key) * 8;
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+                fa[kk][i] = *reinterpret_cast<const bf16x8 *>(&lA[fbA + i * 32 * BK + ch]);
+#pragma unroll
+            for (int j = 0; j < FC; ++j)
+                fb[kk][j] = *reinterpret_cast<const bf16x8 *>(&lB[fbB + j * 32 * BK + ch]);
+        }
+    };
+
+    f32x16 acc[FR][FC];
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FC; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    const int64_t N = g.P / BK;
+    // One stage: M(s) then C(s).  SL = s % S is a compile-time slot; FULL
+    // (s + 3 < N known) drops the run-time checks of the steady loop.
+    auto stage = [&](auto slc, auto fullc, int64_t st) {
+        constexpr int SL = decltype(slc)::value;
+        constexpr bool FULL = decltype(fullc)::value;
+        const std::integral_constant<int, (SL + S - 1) % S> nxc;
+        if (FULL || st + 3 < N)
+            dma(sA(nxc), sB(nxc), st + 3);
+        frag_read(sA(slc), sB(slc));
+        // This wave's loads of stage st+1 have landed once at most the
+        // groups issued after them (stages st+2, st+3) are outstanding.
+        if (FULL || st + 3 < N)
+            vm_wait<8>();
+        else if (st + 2 < N)
+            vm_wait<4>();
+        else
+            vm_wait<0>();
+        pp_barrier();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int j = 0; j < FC; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j],
+                                                                        acc[i][j], 0, 0, 0);
+        pp_barrier();
+    };
+
+    // Prologue: stages 0-2 in flight, wait for stage 0.
+    unroll_seq(std::make_integer_sequence<int, S - 1>{}, [&](auto bc) {
+        if (decltype(bc)::value < N)
+            dma(sA(bc), sB(bc), decltype(bc)::value);
+    });
+    if (N > 2)
+        vm_wait<8>();
+    else if (N > 1)
+        vm_wait<4>();
+    else
+        vm_wait<0>();
+    pp_barrier();
+    if (grp == 1)
+        pp_barrier();
+    int64_t st = 0;
+    const std::true_type full;
+    const std::false_type guarded;
+    for (; st + S + 3 <= N; st += S)
+        unroll_seq(std::make_integer_sequence<int, S>{},
+                   [&](auto bc) { stage(bc, full, st + decltype(bc)::value); });
+    // The loop leaves st % S == 0 with at most S + 2 stages to go.
+    unroll_seq(std::make_integer_sequence<int, S + 2>{}, [&](auto bc) {
+        constexpr int k = decltype(bc)::value;
+        if (st + k < N)
+            stage(std::integral_constant<int, k % S>{}, guarded, st + k);
+    });
+    if (grp == 0)
+        pp_barrier();
+
+    store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + grp * TC, lane);
+}
+
+hipError_t launch_pp(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
+{
+    TileMap tm;
+    tm.tiles_r = static_cast<int>((p.R + 255) / 256);
+    tm.tiles_c = static_cast<int>((p.C + 255) / 256);
+    tm.group_r = group_r < 1 ? 1 : group_r;
+    const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
+    if (nwg == 0)
+        return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(nwg)), block(512);
+    if (epi == Epi::kStoreBF16)
+        hipLaunchKernelGGL((gemm_pp<1>), grid, block, 0, s, p, tm);
+    else
+        hipLaunchKernelGGL((gemm_pp<0>), grid, block, 0, s, p, tm);
+    return hipGetLastError();
+}
+
 template <int BR, int BC, int WR, int WC, bool AT, bool BT>
 hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
@@ -1092,6 +1314,13 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
         return launch_small<64, 6>(p, epi, 8, s);
     if (p.C <= 256)
         return launch_small<128, LMH_SMALL_S128>(p, epi, 8, s);
+    // Many tokens: the ping-pong ring kernel for K <= 8192 (measured 1-3 %
+    // ahead of gemm_big there on MI355X), gemm_big for longer K (2-5 % ahead).
+#ifndef LMH_PP
+#define LMH_PP 1
+#endif
+    if (LMH_PP && p.P % 32 == 0 && p.P <= 8192 && epi != Epi::kAccumF32)
+        return launch_pp(p, epi, 8, s);
     return launch_big<256, 256, 4, 2, false, false>(p, epi, 8, s);
 }
 

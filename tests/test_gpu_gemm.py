@@ -73,10 +73,16 @@ def _up(v, m):
     (1, 8, 1, 0), (3, 24, 5, 8), (17, 72, 65, 0), (33, 200, 130, 16), (130, 64, 257, 8),
     (64, 136, 300, 0), (257, 96, 129, 24), (31, 1000, 511, 0), (40, 8, 1000, 0),
     (7, 13, 9, 0), (19, 77, 33, 8),
+    # many tokens, K a multiple of 32 up to 8192: 1, 2, 7 and 8 stages of 32
+    (260, 32, 300, 0), (300, 64, 260, 8), (270, 224, 513, 0), (512, 256, 520, 8),
+    # many tokens on the 64-wide-stage kernel: K not a multiple of 32, K > 8192
+    (300, 200, 700, 8), (264, 8224, 300, 0),
 ])
 def test_logits_ragged_integer_exact(M, K, V, pad):
     """Ragged M, K, V (partial tiles on every edge, K not a multiple of the
-    64-wide stage nor of 8), padded leading dimensions; padding never written."""
+    64-wide stage nor of 8), padded leading dimensions; padding never written.
+    Covers both large-tile kernels: the 32-wide-stage ring (K a multiple of
+    32, K <= 8192) at 1, 2, 7 and 8 stages, and the 64-wide-stage kernel."""
     inp = workloads.integer_gemm(M, K, V, seed=M * 1000 + K + V, with_targets=False)
     _say(f"ragged logits M={M} K={K} V={V} pad={pad}")
     x = dev_bf16(inp.x, _up(K, 8) + pad)
