@@ -61,6 +61,11 @@ def _load():
     lib.orc_xent_bwd.argtypes = [_vp, _i64, _i64, _vp, _i32, _vp, _i64,
                                  _i64, _vp, _vp, ctypes.c_int]
     lib.orc_xent_bwd.restype = ctypes.c_int
+    lib.orc_xent_partial.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _vp,
+                                     ctypes.c_int]
+    lib.orc_xent_partial.restype = ctypes.c_int
+    lib.orc_xent_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]
+    lib.orc_xent_merge.restype = None
     lib.orc_xent_mean.argtypes = [_vp, _vp, _i32, _i64, _vp]
     lib.orc_xent_mean.restype = ctypes.c_int
     lib.orc_round_bf16_array.argtypes = [_vp, _i64, _vp]
@@ -179,6 +184,39 @@ def xent_fwd(z, target, ignore_index=-100, rows=None, nthreads=None):
                               _ptr(r), _ptr(st), _nthreads(nthreads))
     if rc != 0:
         raise ValueError(f"orc_xent_fwd failed ({rc}): target out of range?")
+    return st
+
+
+def xent_partial(z, target, ignore_index=-100, col0=0, block_cols=4096, rows=None, nthreads=None):
+    """Partial statistics of a slice of logits rows z [n, ncols] that holds
+    the global columns [col0, col0 + ncols), in blocks of block_cols columns:
+    an array [n_blocks, n_sel, 4] of {m_b, d_b, X_b, own_b} (FP64)."""
+    z, ld = _rowmajor(z, np.float32, "logits")
+    t = np.ascontiguousarray(np.asarray(target, dtype=np.int32))
+    n, nc = z.shape
+    if t.shape != (n,):
+        raise ValueError("target must be [n_rows]")
+    r, nsel = _rows_arg(rows, n)
+    nb = (nc + block_cols - 1) // block_cols
+    part = np.empty((nb, nsel, 4), dtype=np.float64)
+    rc = _load().orc_xent_partial(_ptr(z), ld, nc, int(col0), int(block_cols), _ptr(t),
+                                  int(ignore_index), nsel, _ptr(r), _ptr(part),
+                                  _nthreads(nthreads))
+    if rc != 0:
+        raise ValueError(f"orc_xent_partial failed ({rc})")
+    return part
+
+
+def xent_merge(part, target, vocab, ignore_index=-100):
+    """Merge partial records part [n_parts, n, 4] (FP64) into stats [n, 4] =
+    {m, d, X_y, loss}; unowned or out-of-range targets give NaN X and loss."""
+    p = np.ascontiguousarray(np.asarray(part, dtype=np.float64))
+    t = np.ascontiguousarray(np.asarray(target, dtype=np.int32))
+    if p.ndim != 3 or p.shape[2] != 4 or p.shape[1] != t.size:
+        raise ValueError("part must be [n_parts, n_rows, 4]")
+    st = np.empty((t.size, 4), dtype=np.float64)
+    _load().orc_xent_merge(_ptr(p), p.shape[0], 4 * t.size, t.size, _ptr(t), int(ignore_index),
+                           int(vocab), _ptr(st))
     return st
 
 

@@ -27,6 +27,14 @@
  *   CE bwd g_j = dloss * (exp(z_j - m) / d - [j == y]); ignored rows are 0.
  *   mean   n_valid = #{y != ignore}, mean = sum loss / n_valid,
  *          inv = 1 / n_valid (both 0 when n_valid == 0).
+ *   split  per column block b of a row: m_b = max z_j, d_b = sum exp(z_j - m_b)
+ *          over the block, X_b = z_y and own_b = 1 when the (global) target
+ *          column lies in the block, else X_b = own_b = 0; merged over the
+ *          blocks of a row: m = max m_b, d = sum d_b exp(m_b - m), X from the
+ *          one owning block, loss = (m - X) + log d.  This is the per-shard
+ *          form of the statistics of vocabulary-parallel cross entropy
+ *          ([XENT] "Description" names Megatron's vocabulary-parallel CE as
+ *          the FP32 reference): exp(z_j - m) = exp(z_j - m_b) exp(m_b - m).
  * The softmax-minus-one-hot form of the backward is the derivative of the
  * forward loss; the tests pin it by finite differences of the forward.
  *
@@ -294,6 +302,107 @@ int orc_xent_bwd(const float *z, int64_t ld, int64_t V, const int32_t *tgt,
     c.rows = rows, c.dloss = dloss, c.dloss_stride = dloss_stride, c.g = g;
     orc_parallel_rows(orc_xent_bwd_rows, &c, n_out_rows, nthreads);
     return c.bad ? -3 : 0;
+}
+
+/* ------------------------------------------ split-vocabulary cross entropy */
+
+typedef struct {
+    const float *z;
+    int64_t ld, ncols, col0, bc, nb;
+    const int32_t *tgt;
+    int32_t ignore_index;
+    const int64_t *rows;
+    int64_t n_out;
+    double *part;
+} orc_part_ctx;
+
+static void orc_xent_partial_rows(void *vctx, int64_t r0, int64_t r1)
+{
+    orc_part_ctx *c = (orc_part_ctx *)vctx;
+    for (int64_t r = r0; r < r1; ++r) {
+        int64_t i = c->rows ? c->rows[r] : r;
+        const float *z = c->z + i * c->ld;
+        int32_t y = c->tgt[i];
+        for (int64_t b = 0; b < c->nb; ++b) {
+            int64_t j0 = b * c->bc;
+            int64_t j1 = j0 + c->bc < c->ncols ? j0 + c->bc : c->ncols;
+            double m = -INFINITY;
+            for (int64_t j = j0; j < j1; ++j)
+                if ((double)z[j] > m)
+                    m = (double)z[j];
+            double d = 0.0;
+            for (int64_t j = j0; j < j1; ++j)
+                d += exp((double)z[j] - m);
+            double x = 0.0, own = 0.0;
+            if (y != c->ignore_index) {
+                int64_t loc = (int64_t)y - c->col0; /* column within the slice */
+                if (loc >= j0 && loc < j1) {
+                    x = (double)z[loc];
+                    own = 1.0;
+                }
+            }
+            double *pp = c->part + 4 * (b * c->n_out + r);
+            pp[0] = m, pp[1] = d, pp[2] = x, pp[3] = own;
+        }
+    }
+}
+
+/* Partial statistics of a slice of a logits row holding the global columns
+ * [col0, col0 + ncols), split into blocks of bc columns (the last one
+ * shorter): part[b][r] = {m_b, d_b, X_b, own_b} for row i_r (FP64). */
+int orc_xent_partial(const float *z, int64_t ld, int64_t ncols, int64_t col0, int64_t bc,
+                     const int32_t *tgt, int32_t ignore_index, int64_t n_out_rows,
+                     const int64_t *rows, double *part, int nthreads)
+{
+    if (n_out_rows < 0 || ncols < 1 || ld < ncols || bc < 1 || col0 < 0)
+        return -1;
+    orc_part_ctx c;
+    memset(&c, 0, sizeof c);
+    c.z = z, c.ld = ld, c.ncols = ncols, c.col0 = col0, c.bc = bc;
+    c.nb = (ncols + bc - 1) / bc;
+    c.tgt = tgt, c.ignore_index = ignore_index, c.rows = rows, c.n_out = n_out_rows;
+    c.part = part;
+    orc_parallel_rows(orc_xent_partial_rows, &c, n_out_rows, nthreads);
+    return 0;
+}
+
+/* Merge n_parts partial records per row (part + p * part_stride + 4 r) into
+ * stats[r] = {m, d, X_y, loss}.  Ignored rows: X = loss = 0.  A target
+ * outside [0, vocab), or one not owned by exactly one part, gives X = loss =
+ * NaN (m and d are still the merged values). */
+void orc_xent_merge(const double *part, int64_t n_parts, int64_t part_stride, int64_t n_rows,
+                    const int32_t *tgt, int32_t ignore_index, int64_t vocab, double *stats)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        double m = -INFINITY;
+        for (int64_t p = 0; p < n_parts; ++p)
+            if (part[p * part_stride + 4 * r] > m)
+                m = part[p * part_stride + 4 * r];
+        double d = 0.0, x = 0.0;
+        int64_t owners = 0;
+        for (int64_t p = 0; p < n_parts; ++p) {
+            const double *pp = part + p * part_stride + 4 * r;
+            d += pp[1] * exp(pp[0] - m);
+            if (pp[3] != 0.0) {
+                x = pp[2];
+                ++owners;
+            }
+        }
+        double *st = stats + 4 * r;
+        st[0] = m;
+        st[1] = d;
+        int32_t y = tgt[r];
+        if (y == ignore_index) {
+            st[2] = 0.0;
+            st[3] = 0.0;
+        } else if (y < 0 || (int64_t)y >= vocab || owners != 1) {
+            st[2] = NAN;
+            st[3] = NAN;
+        } else {
+            st[2] = x;
+            st[3] = (m - x) + log(d);
+        }
+    }
 }
 
 /* out = {mean over non-ignored rows, 1 / n_valid, n_valid}; zeros if none. */

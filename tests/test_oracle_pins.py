@@ -294,6 +294,107 @@ def test_xent_bwd_per_row_vs_scalar_dloss():
 
 # ----------------------------------------------------------------- mean pins
 
+# ------------------------------------------------ split-vocabulary CE pins
+
+def _split_inputs(n, V, seed, ignore_frac=0.2):
+    rng = np.random.default_rng(seed)
+    z = (rng.normal(0.0, 2.0, (n, V)) + rng.choice([0.0, 25.0], (n, V), p=[0.97, 0.03]))
+    z = z.astype(np.float32)
+    t = rng.integers(0, V, n).astype(np.int32)
+    t[rng.random(n) < ignore_frac] = -100
+    return z, t
+
+
+@pytest.mark.parametrize("V,bc", [(1, 4), (7, 1), (37, 4), (100, 32), (257, 64), (1000, 999),
+                                  (1000, 1000), (64, 4096)])
+def test_split_merge_equals_full_row(V, bc):
+    """Invariant: the merge of the per-block records equals the full-row
+    statistics of the (separately pinned) forward, for ragged last blocks,
+    one-column blocks and a single block wider than the row."""
+    z, t = _split_inputs(9, V, seed=V * 31 + bc)
+    part = oracle.xent_partial(z, t, -100, col0=0, block_cols=bc)
+    assert part.shape == (-(-V // bc), 9, 4)
+    st = oracle.xent_merge(part, t, V, -100)
+    ref = oracle.xent_fwd(z, t, -100)
+    assert np.array_equal(st[:, 0], ref[:, 0])          # max of maxima is exact
+    assert np.array_equal(st[:, 2], ref[:, 2])          # X_y copied, not computed
+    np.testing.assert_allclose(st[:, 1], ref[:, 1], rtol=1e-13, atol=0)
+    np.testing.assert_allclose(st[:, 3], ref[:, 3], rtol=1e-12, atol=1e-12)
+
+
+def test_split_slices_with_column_offset():
+    """Two slices of the vocabulary (global columns [0, a) and [a, V)), each
+    reduced with its own col0 and targets given as global columns, merge to
+    the full-row statistics; each valid target is owned by exactly one slice."""
+    V, a = 300, 128
+    z, t = _split_inputs(11, V, seed=5)
+    p0 = oracle.xent_partial(np.ascontiguousarray(z[:, :a]), t, -100, col0=0, block_cols=64)
+    p1 = oracle.xent_partial(np.ascontiguousarray(z[:, a:]), t, -100, col0=a, block_cols=48)
+    part = np.concatenate([p0, p1])
+    owners = part[:, :, 3].sum(axis=0)
+    assert np.array_equal(owners, np.where(t == -100, 0.0, 1.0))
+    st = oracle.xent_merge(part, t, V, -100)
+    ref = oracle.xent_fwd(z, t, -100)
+    assert np.array_equal(st[:, 0], ref[:, 0]) and np.array_equal(st[:, 2], ref[:, 2])
+    np.testing.assert_allclose(st[:, 1], ref[:, 1], rtol=1e-13, atol=0)
+    # merge order does not change the statistics (m exactly)
+    st_rev = oracle.xent_merge(part[::-1].copy(), t, V, -100)
+    assert np.array_equal(st_rev[:, 0], st[:, 0]) and np.array_equal(st_rev[:, 2], st[:, 2])
+    np.testing.assert_allclose(st_rev[:, 1], st[:, 1], rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("c", [0.0, -3.5, 11.25])
+def test_split_uniform_closed_form(c):
+    """All logits equal: m_b = c and d_b = the block's width exactly; the
+    owning block is (y - col0) // block_cols."""
+    V, bc = 1000, 96
+    z = np.full((4, V), c, dtype=np.float32)
+    t = np.array([0, 999, 96, -100], dtype=np.int32)
+    part = oracle.xent_partial(z, t, -100, block_cols=bc)
+    widths = np.minimum(bc, V - bc * np.arange(part.shape[0]))
+    assert np.all(part[:, :, 0] == c)
+    assert np.array_equal(part[:, :, 1], np.repeat(widths[:, None].astype(np.float64), 4, axis=1))
+    own = part[:, :, 3]
+    for r, y in enumerate(t):
+        expect = np.zeros(part.shape[0])
+        if y != -100:
+            expect[y // bc] = 1.0
+        assert np.array_equal(own[:, r], expect)
+        assert np.all(part[:, r, 2] == (c if y != -100 else 0.0) * own[:, r])
+
+
+def test_split_single_column_blocks_and_unshifted_sum():
+    """One-column blocks: m_b = z_j, d_b = 1 exactly.  Wider blocks of small
+    logits: d_b * exp(m_b) equals the unshifted sum of exp(z_j) (brute force
+    without the max shift)."""
+    rng = np.random.default_rng(3)
+    z = rng.uniform(-4, 4, (3, 10)).astype(np.float32)
+    t = np.array([2, 9, 0], dtype=np.int32)
+    p1 = oracle.xent_partial(z, t, -100, block_cols=1)
+    assert np.array_equal(p1[:, :, 0].T, z.astype(np.float64))
+    assert np.all(p1[:, :, 1] == 1.0)
+    p4 = oracle.xent_partial(z, t, -100, block_cols=4)
+    for b in range(3):
+        blk = z[:, 4 * b:4 * b + 4].astype(np.float64)
+        brute = np.array([sum(math.exp(v) for v in row) for row in blk])
+        np.testing.assert_allclose(p4[b, :, 1] * np.exp(p4[b, :, 0]), brute, rtol=1e-14)
+
+
+def test_split_merge_bad_and_unowned_targets():
+    """Ignored rows: X = loss = 0.  A target outside [0, vocab), or one that no
+    supplied part owns, gives NaN X and loss while m and d stay finite."""
+    V = 50
+    z, _ = _split_inputs(4, V, seed=9, ignore_frac=0.0)
+    t = np.array([-100, 60, 10, 45], dtype=np.int32)
+    part = oracle.xent_partial(np.ascontiguousarray(z[:, :40]), t, -100, block_cols=16)
+    st = oracle.xent_merge(part, t, V, -100)            # columns 40..49 not supplied
+    assert st[0, 2] == 0.0 and st[0, 3] == 0.0
+    assert np.isnan(st[1, 2]) and np.isnan(st[1, 3])    # 60 >= vocab
+    assert np.isfinite(st[2, 3]) and st[2, 2] == np.float64(z[2, 10])
+    assert np.isnan(st[3, 2]) and np.isnan(st[3, 3])    # 45 owned by no part
+    assert np.all(np.isfinite(st[:, :2]))
+
+
 def test_xent_mean():
     loss = np.array([1.5, 9.0, 2.25, 4.0, 0.5])
     t = np.array([3, -100, 1, -100, 0], np.int32)
