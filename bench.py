@@ -317,7 +317,47 @@ def main():
             "bwd_inplace_gbps": bwd_b / (bwdip_ms * 1e-3) / 1e9,
         }
         log(f"[bench] CE fwd {fwd_ms:.3f} ms bwd {bwd_ms:.3f} ms -> {ce_gbps:.0f} GB/s")
-        del z, g32
+        del g32
+        # Split-vocabulary forward (per-block partial statistics + merge) beside
+        # the one-pass forward: the 8192 x 131072 logits above, and N(0, 3^2)
+        # logits of 128 and 1024 rows x 32768 (few rows: one workgroup per row
+        # leaves most of the 256 CUs idle).
+        log("[bench] CE forward: one pass vs split vocabulary (4096-column blocks)")
+        split = {}
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(workloads.SEED)
+        for n_s, v_s in ((128, 32768), (1024, 32768), (n_ce, v_ce)):
+            if (n_s, v_s) == (n_ce, v_ce):
+                zs, ts = z, ct
+            else:
+                zs = torch.randn((n_s, v_s), device="cuda", generator=gen) * 3.0
+                ts = torch.randint(0, v_s, (n_s,), device="cuda", generator=gen,
+                                   dtype=torch.int32)
+            ls = torch.empty((n_s,), dtype=torch.float32, device="cuda")
+            ss = torch.empty((n_s, 4), dtype=torch.float32, device="cuda")
+            nb_s = (v_s + 4095) // 4096
+            ps = torch.empty((nb_s, n_s, 4), dtype=torch.float32, device="cuda")
+            one = lambda: lmh.lmhead_xent_fwd(zs, ts, -100, loss=ls, stats=ss)
+            two = lambda: (lmh.lmhead_xent_partial(zs, ts, -100, block_cols=4096, part=ps),
+                           lmh.lmhead_xent_merge(ps, ts, v_s, -100, loss=ls, stats=ss))
+            for _ in range(3):
+                one()
+                two()
+            stm = KernelTimer(torch)
+            for i in range(args.samples):
+                for name, fn in ((("one", one), ("split", two)) if i % 2 == 0
+                                 else (("split", two), ("one", one))):
+                    stm(name, fn)
+            torch.cuda.synchronize()
+            by = 4.0 * n_s * v_s + 24 * n_s
+            t1, t2 = statistics.median(stm.ms("one")), statistics.median(stm.ms("split"))
+            split[f"{n_s}x{v_s}"] = {"one_pass_ms": t1, "split_ms": t2,
+                                     "one_pass_gbps": by / (t1 * 1e-3) / 1e9,
+                                     "split_gbps": by / (t2 * 1e-3) / 1e9}
+            log(f"[bench]   {n_s}x{v_s}: one pass {t1 * 1e3:.1f} us, split {t2 * 1e3:.1f} us")
+            del zs, ts, ls, ss, ps
+        out["xent_fwd_split_vocab"] = split
+        del z
 
     # ------------------------------------------ counter calibration copy
     if args.calib_copy_mib > 0:

@@ -106,6 +106,61 @@ int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t
                         float *loss, float *stats, void *stream);
 
 /*
+ * lmhead_xent_partial -- split-vocabulary CE forward, step 1        ([XENT])
+ *
+ *  The per-shard half of vocabulary-parallel cross entropy ([XENT],
+ *  "Description", names Megatron's vocabulary-parallel CE as the FP32
+ *  reference): the statistics of a slice of each logits row, per column
+ *  block, to be combined by lmhead_xent_merge.  The same call serves a vocab
+ *  shard of a larger model (col0 = the shard's first global column) and a
+ *  single GPU that splits long rows into blocks so that few rows still fill
+ *  the chip.
+ *
+ *  logits  FP32 [n_rows x n_cols], leading dimension ld; the slice holds the
+ *          global columns [col0, col0 + n_cols).  Read once.
+ *  block_cols  columns per block, a positive multiple of 4; the slice is cut
+ *          into n_blocks = ceil(n_cols / block_cols) blocks (the last one may
+ *          be shorter).  n_blocks * n_rows must not exceed INT32_MAX.
+ *  target  int32 [n_rows], GLOBAL column indices; ignore_index as in the
+ *          forward.
+ *  part    FP32 output, n_blocks arrays of n_rows 16-byte records:
+ *          part[b * part_stride + 4 i + {0,1,2,3}] =
+ *            { m_b   = max of the row's block,
+ *              d_b   = sum over the block of exp(z - m_b),
+ *              X_b   = the target logit if col0 <= target_i - b block_cols
+ *                      < col0 + (width of block b), else 0,
+ *              own_b = 1 in that case, else 0 }   (ignored rows: X = own = 0).
+ *          part_stride (elements) >= 4 n_rows and a multiple of 4.  part must
+ *          not overlap the logits or the target.
+ */
+int32_t lmhead_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                            int64_t col0, int64_t block_cols, const int32_t *target,
+                            int32_t ignore_index, float *part, int64_t part_stride,
+                            void *stream);
+
+/*
+ * lmhead_xent_merge -- split-vocabulary CE forward, step 2          ([XENT])
+ *
+ *  Combines n_parts partial records per row (from one or more
+ *  lmhead_xent_partial calls, at part + p * part_stride + 4 i for part p) in
+ *  the order p = 0, 1, ... (a running maximum, rescaled as it grows):  m = max m_p,
+ *  d = sum_p d_p exp(m_p - m),  X_y
+ *  from the one part that owns the target,  loss = (m - X_y) + log d.
+ *  Writes the same stats record and loss as lmhead_xent_fwd, so that
+ *  lmhead_xent_bwd can run on the merged statistics.
+ *
+ *  vocab   total number of columns; a target outside [0, vocab) that is not
+ *          ignore_index, or one owned by no part or by several, gives
+ *          X = loss = NaN (m and d are still merged).  Ignored rows: X = loss = 0.
+ *  loss    FP32 [n_rows] or NULL;  stats FP32 [n_rows x 4].
+ *  n_parts >= 1, vocab >= 1, part_stride >= 4 n_rows and a multiple of 4.
+ *  stats and loss must not overlap the parts or the target.
+ */
+int32_t lmhead_xent_merge(const float *part, int64_t n_parts, int64_t part_stride,
+                          int64_t n_rows, const int32_t *target, int32_t ignore_index,
+                          int64_t vocab, float *loss, float *stats, void *stream);
+
+/*
  * lmhead_xent_mean -- mean reduction of the per-row loss
  *
  *  loss     FP32 [n_rows]; target int32 [n_rows] (rows equal to ignore_index

@@ -41,6 +41,8 @@ _SIGNATURES = {
     "lmhead_version": ([], _i32),
     "lmhead_logits": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
     "lmhead_xent_fwd": ([_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp], _i32),
+    "lmhead_xent_partial": ([_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _vp], _i32),
+    "lmhead_xent_merge": ([_vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _vp], _i32),
     "lmhead_xent_mean": ([_vp, _vp, _i32, _i64, _vp, _vp, _vp], _i32),
     "lmhead_xent_bwd": ([_vp, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _i64, _i32, _i64, _i64,
                          _vp], _i32),
@@ -189,6 +191,56 @@ def lmhead_xent_fwd(logits, target, ignore_index=-100, loss=None, stats=None, st
     _check("lmhead_xent_fwd", lib().lmhead_xent_fwd(pz, ld, n, V, pt, int(ignore_index), pl, ps,
                                                     _stream(stream)))
     return (loss if loss is not False else None), stats
+
+
+def lmhead_xent_partial(logits, target, ignore_index=-100, col0=0, block_cols=4096, part=None,
+                        stream=None):
+    """Split-vocabulary CE forward, step 1: per column block of each row,
+    {m_b, d_b, X_b, own_b}.  The logits slice holds the global columns
+    [col0, col0 + n_cols); targets are global.  Returns part [n_blocks,
+    n_rows, 4] (any [n_blocks, n_rows, 4] FP32 view with a contiguous last
+    two dimensions may be passed in)."""
+    pz, ld = _mat(logits, "logits", torch.float32)
+    n, nc = logits.shape
+    pt = _vec(target, "target", torch.int32, n)
+    nb = max((nc + block_cols - 1) // block_cols, 1) if block_cols > 0 else 1
+    if part is None:
+        part = torch.empty((nb, n, STATS_COLS), dtype=torch.float32, device=logits.device)
+    pp, stride = _parts(part, n)
+    _check("lmhead_xent_partial",
+           lib().lmhead_xent_partial(pz, ld, n, nc, int(col0), int(block_cols), pt,
+                                     int(ignore_index), pp, stride, _stream(stream)))
+    return part
+
+
+def lmhead_xent_merge(part, target, vocab, ignore_index=-100, loss=None, stats=None, stream=None):
+    """Split-vocabulary CE forward, step 2: merge part [n_parts, n_rows, 4]
+    into (loss [n], stats [n, 4] = {m, d, X_y, loss}), as lmhead_xent_fwd."""
+    n = target.numel()
+    pt = _vec(target, "target", torch.int32, n)
+    pp, stride = _parts(part, n)
+    if stats is None:
+        stats = _empty((n, STATS_COLS), torch.float32, part)
+    if loss is None:
+        loss = _empty((n,), torch.float32, part)
+    ps = _vec(stats, "stats", torch.float32, n * STATS_COLS)
+    pl = _vec(loss, "loss", torch.float32, n) if loss is not False else None
+    _check("lmhead_xent_merge",
+           lib().lmhead_xent_merge(pp, part.shape[0], stride, n, pt, int(ignore_index), int(vocab),
+                                   pl, ps, _stream(stream)))
+    return (loss if loss is not False else None), stats
+
+
+def _parts(part, n):
+    """(pointer, stride between parts in elements) of an FP32 [P, n, 4] tensor."""
+    if not isinstance(part, torch.Tensor) or not part.is_cuda or part.dtype != torch.float32:
+        raise TypeError("part: expected a GPU float32 tensor")
+    if part.dim() != 3 or part.shape[1] != n or part.shape[2] != STATS_COLS:
+        raise ValueError(f"part: expected shape [n_parts, {n}, {STATS_COLS}]")
+    if n > 0 and (part.stride(2) != 1 or part.stride(1) != STATS_COLS):
+        raise ValueError("part: each part must be a contiguous [n_rows, 4] block")
+    stride = part.stride(0) if part.shape[0] > 1 else STATS_COLS * n
+    return _vp(part.data_ptr()), int(stride)
 
 
 def lmhead_xent_mean(loss, target, ignore_index=-100, mean=None, inv_nvalid=None, stream=None):

@@ -97,7 +97,7 @@ const char *lmhead_status_str(int32_t status)
 
 int32_t lmhead_version(void)
 {
-    return 100;
+    return 101;
 }
 
 int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, void *out,
@@ -159,6 +159,64 @@ int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t
     }
     return launch_status(lmh::launch_xent_fwd(logits, ld, n_rows, n_cols, target, ignore_index,
                                               loss, stats, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                            int64_t col0, int64_t block_cols, const int32_t *target,
+                            int32_t ignore_index, float *part, int64_t part_stride,
+                            void *stream)
+{
+    if (n_rows < 0 || n_cols < 0 || n_rows > kMaxDim || n_cols > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (n_rows == 0)
+        return LMH_OK;
+    if (n_cols < 1 || col0 < 0 || col0 > kMaxDim || block_cols < 4 || block_cols % 4 != 0)
+        return LMH_ERR_SHAPE;
+    LMH_TRY(check_matrix(logits, n_rows, n_cols, ld, 4));
+    const int64_t nb = (n_cols + block_cols - 1) / block_cols;
+    if (nb > kMaxDim / n_rows || part_stride < 4 * n_rows)
+        return LMH_ERR_SHAPE;
+    if (!target || !part)
+        return LMH_ERR_NULL;
+    if (!aligned16(part) || part_stride % 4 != 0 || !aligned4(target))
+        return LMH_ERR_ALIGN;
+    const Span sp = span_of(part, nb, 4 * n_rows, part_stride, 4);
+    if (overlaps(sp, span_of(logits, n_rows, n_cols, ld, 4)) ||
+        overlaps(sp, span_of(target, 1, n_rows, n_rows, 4)))
+        return LMH_ERR_ALIAS;
+    return launch_status(lmh::launch_xent_partial(logits, ld, n_rows, n_cols, col0, block_cols,
+                                                  target, ignore_index, part, part_stride,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_xent_merge(const float *part, int64_t n_parts, int64_t part_stride,
+                          int64_t n_rows, const int32_t *target, int32_t ignore_index,
+                          int64_t vocab, float *loss, float *stats, void *stream)
+{
+    if (n_rows < 0 || n_rows > kMaxDim || n_parts < 0 || n_parts > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (n_rows == 0)
+        return LMH_OK;
+    if (n_parts < 1 || vocab < 1 || part_stride < 4 * n_rows)
+        return LMH_ERR_SHAPE;
+    if (!part || !target || !stats)
+        return LMH_ERR_NULL;
+    if (!aligned16(part) || part_stride % 4 != 0 || !aligned16(stats) || !aligned4(target) ||
+        (loss && !aligned4(loss)))
+        return LMH_ERR_ALIGN;
+    const Span sp = span_of(part, n_parts, 4 * n_rows, part_stride, 4);
+    const Span st = span_of(target, 1, n_rows, n_rows, 4);
+    const Span ss = span_of(stats, n_rows, 4, 4, 4);
+    if (overlaps(ss, sp) || overlaps(ss, st))
+        return LMH_ERR_ALIAS;
+    if (loss) {
+        const Span sl = span_of(loss, 1, n_rows, n_rows, 4);
+        if (overlaps(sl, sp) || overlaps(sl, st) || overlaps(sl, ss))
+            return LMH_ERR_ALIAS;
+    }
+    return launch_status(lmh::launch_xent_merge(part, n_parts, part_stride, n_rows, target,
+                                                ignore_index, vocab, loss, stats,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int32_t lmhead_xent_mean(const float *loss, const int32_t *target, int32_t ignore_index,

@@ -22,6 +22,10 @@
 #include <math.h>
 
 namespace lmh {
+#ifndef LMH_XF_PF
+#define LMH_XF_PF 1
+#endif
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -84,28 +88,43 @@ __device__ __forceinline__ float max4(const float4 &v)
     return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
 }
 
+// Reduce columns [0, ncols) of one row (16-byte aligned start) to the pair
+// (m, d) = (max z, sum exp(z - m)); the result is valid in thread 0.  Each
+// thread keeps a running pair over U 16-byte loads at a time (one rescale per
+// 4U values), then a wavefront butterfly and a fixed-order cross-wave merge.
 template <int NT, int U, bool NTL>
-__global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ z, int64_t ld,
-                                                      int64_t V, const int32_t *__restrict__ tgt,
-                                                      int32_t ignore_index, float *__restrict__ loss,
-                                                      float4 *__restrict__ stats)
+__device__ __forceinline__ void reduce_row_md(const float *zr, int64_t ncols, int tid,
+                                              float &m_out, float &d_out)
 {
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const float *zr = z + row * ld;
     const float4 *z4 = reinterpret_cast<const float4 *>(zr);
-    const int64_t n4 = V >> 2;
+    const int64_t n4 = ncols >> 2;
 
     float m = -INFINITY, d = 0.0f;
-    for (int64_t base = 0; base < n4; base += static_cast<int64_t>(NT) * U) {
-        if (base + tid >= n4)
-            break;
-        float4 v[U];
+    constexpr int64_t STEP = static_cast<int64_t>(NT) * U;
+    auto load_group = [&](float4 (&v)[U], int64_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = base + u * NT + tid;
             v[u] = (i < n4) ? ld4<NTL>(z4 + i)
                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+    };
+    float4 nxt[U];
+    if (LMH_XF_PF && tid < n4)
+        load_group(nxt, 0);
+    for (int64_t base = 0; base < n4; base += STEP) {
+        if (base + tid >= n4)
+            break;
+        float4 v[U];
+        if (LMH_XF_PF) {
+            // The next group's loads go out before this group is reduced.
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = nxt[u];
+            if (base + STEP + tid < n4)
+                load_group(nxt, base + STEP);
+        } else {
+            load_group(v, base);
         }
         float bm = max4(v[0]);
 #pragma unroll
@@ -123,10 +142,10 @@ __global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ 
         d = acc;
         m = mn;
     }
-    // Tail: the last V % 4 columns, one per thread.
+    // Tail: the last ncols % 4 columns, one per thread.
     {
         const int64_t j = 4 * n4 + tid;
-        if (tid < 4 && j < V) {
+        if (tid < 4 && j < ncols) {
             const float t = zr[j];
             const float mn = fmaxf(m, t);
             d = d * exp_shifted(m, mn) + exp_shifted(t, mn);
@@ -153,6 +172,23 @@ __global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ 
         d = sd[0];
         for (int w = 1; w < NW; ++w)
             merge_md(m, d, sm[w], sd[w]);
+    }
+    m_out = m;
+    d_out = d;
+}
+
+template <int NT, int U, bool NTL>
+__global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ z, int64_t ld,
+                                                      int64_t V, const int32_t *__restrict__ tgt,
+                                                      int32_t ignore_index, float *__restrict__ loss,
+                                                      float4 *__restrict__ stats)
+{
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *zr = z + row * ld;
+    float m, d;
+    reduce_row_md<NT, U, NTL>(zr, V, tid, m, d);
+    if (tid == 0) {
         const int32_t y = tgt[row];
         float x, l;
         if (y == ignore_index) {
@@ -169,6 +205,103 @@ __global__ __launch_bounds__(NT) void xent_fwd_kernel(const float *__restrict__ 
         if (loss)
             loss[row] = l;
     }
+}
+
+// Split-vocabulary forward, part 1: one workgroup per (row, column block).
+// The slice holds the global columns [col0, col0 + ncols); block b covers its
+// columns [b bc, min((b+1) bc, ncols)).  Record {m_b, d_b, X_b, own_b}: own_b
+// = 1 and X_b = the target logit when the row's (global) target falls in the
+// block, else 0 and 0.
+template <int NT, int U, bool NTL>
+__global__ __launch_bounds__(NT) void xent_partial_kernel(const float *__restrict__ z, int64_t ld,
+                                                          int64_t ncols, int64_t col0, int64_t bc,
+                                                          int64_t nb,
+                                                          const int32_t *__restrict__ tgt,
+                                                          int32_t ignore_index,
+                                                          float4 *__restrict__ part,
+                                                          int64_t part_stride4)
+{
+    const int64_t bid = blockIdx.x;
+    const int64_t row = bid / nb;
+    const int64_t b = bid - row * nb;
+    const int tid = threadIdx.x;
+    const int64_t j0 = b * bc;
+    const int64_t w = min(bc, ncols - j0);
+    const float *zb = z + row * ld + j0;
+    float m, d;
+    reduce_row_md<NT, U, NTL>(zb, w, tid, m, d);
+    if (tid == 0) {
+        const int32_t y = tgt[row];
+        float x = 0.0f, own = 0.0f;
+        if (y != ignore_index) {
+            const int64_t loc = static_cast<int64_t>(y) - col0 - j0;
+            if (loc >= 0 && loc < w) {
+                x = zb[loc];
+                own = 1.0f;
+            }
+        }
+        part[b * part_stride4 + row] = make_float4(m, d, x, own);
+    }
+}
+
+// Split-vocabulary forward, part 2: one thread per row merges the n_parts
+// records in order p = 0, 1, ..., eight at a time (the eight loads are issued
+// before any is used): the running pair (m, d) is rescaled to each chunk's
+// new maximum, so that m = max m_p and d = sum d_p exp(m_p - m); X_y comes
+// from the single owning part.  Writes the same {m, d, X_y, loss} record as
+// xent_fwd_kernel.  No owner, several owners or a target outside [0, vocab):
+// X_y = loss = NaN.
+__global__ __launch_bounds__(256) void xent_merge_kernel(const float4 *__restrict__ part,
+                                                         int64_t n_parts, int64_t part_stride4,
+                                                         int64_t n_rows,
+                                                         const int32_t *__restrict__ tgt,
+                                                         int32_t ignore_index, int64_t vocab,
+                                                         float *__restrict__ loss,
+                                                         float4 *__restrict__ stats)
+{
+    constexpr int C = 8;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (row >= n_rows)
+        return;
+    float m = -INFINITY, d = 0.0f, x = 0.0f;
+    int64_t owners = 0;
+    for (int64_t p0 = 0; p0 < n_parts; p0 += C) {
+        float4 q[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c)  // past the last part: an empty record
+            q[c] = (p0 + c < n_parts) ? part[(p0 + c) * part_stride4 + row]
+                                      : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+        float cm = q[0].x;
+#pragma unroll
+        for (int c = 1; c < C; ++c)
+            cm = fmaxf(cm, q[c].x);
+        const float mn = fmaxf(m, cm);
+        float acc = d * exp_shifted(m, mn);  // first chunk: 0 * exp2(-inf) = 0
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            acc += q[c].y * exp_shifted(q[c].x, mn);
+            if (q[c].w != 0.0f) {
+                x = q[c].z;
+                ++owners;
+            }
+        }
+        d = acc;
+        m = mn;
+    }
+    const int32_t y = tgt[row];
+    float l;
+    if (y == ignore_index) {
+        x = 0.0f;
+        l = 0.0f;
+    } else if (y < 0 || static_cast<int64_t>(y) >= vocab || owners != 1) {
+        x = __int_as_float(0x7fc00000);
+        l = x;
+    } else {
+        l = (m - x) + logf(d);
+    }
+    stats[row] = make_float4(m, d, x, l);
+    if (loss)
+        loss[row] = l;
 }
 
 // Gradient of one row chunk.  OUTBF16 selects the store type only; the FP32
@@ -338,6 +471,34 @@ hipError_t launch_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int6
                            dim3(static_cast<unsigned>(n_rows)), dim3(256), 0, s, logits, ld, n_cols,
                            target, ignore_index, loss, st);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                               int64_t col0, int64_t block_cols, const int32_t *target,
+                               int32_t ignore_index, float *part, int64_t part_stride,
+                               hipStream_t s)
+{
+    if (n_rows == 0)
+        return hipSuccess;
+    const int64_t nb = (n_cols + block_cols - 1) / block_cols;
+    hipLaunchKernelGGL((xent_partial_kernel<256, LMH_XF_U, LMH_XF_NTL>),
+                       dim3(static_cast<unsigned>(nb * n_rows)), dim3(256), 0, s, logits, ld,
+                       n_cols, col0, block_cols, nb, target, ignore_index,
+                       reinterpret_cast<float4 *>(part), part_stride / 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_xent_merge(const float *part, int64_t n_parts, int64_t part_stride,
+                             int64_t n_rows, const int32_t *target, int32_t ignore_index,
+                             int64_t vocab, float *loss, float *stats, hipStream_t s)
+{
+    if (n_rows == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(xent_merge_kernel, dim3(static_cast<unsigned>((n_rows + 255) / 256)),
+                       dim3(256), 0, s, reinterpret_cast<const float4 *>(part), n_parts,
+                       part_stride / 4, n_rows, target, ignore_index, vocab, loss,
+                       reinterpret_cast<float4 *>(stats));
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert lmh.lmhead_version() == 100
+    assert lmh.lmhead_version() == 101
     assert lmh.lmhead_status_str(0) == "LMH_OK"
     for s in range(1, 7):
         assert lmh.lmhead_status_str(s).startswith("LMH_ERR_")
@@ -94,6 +94,51 @@ def test_xent_fwd_validation(L):
     assert f(A, 1024, 8, 1024, B, -100, A, D, None) == ALIAS          # loss over logits
     assert f(A, 1024, 8, 1024, B, -100, D + 16, D, None) == ALIAS     # loss over stats
     assert f(None, 1024, 0, 1024, None, -100, None, None, None) == OK
+
+
+def test_xent_partial_validation(L):
+    f = L.lmhead_xent_partial
+    # (logits, ld, n_rows, n_cols, col0, block_cols, target, ignore, part, part_stride, stream)
+    assert f(A, 1024, -1, 1024, 0, 256, B, -100, C, 32, None) == SHAPE
+    assert f(A, 1024, 8, 0, 0, 256, B, -100, C, 32, None) == SHAPE
+    assert f(A, 1024, 8, 1024, -1, 256, B, -100, C, 32, None) == SHAPE      # col0 < 0
+    assert f(A, 1024, 8, 1024, 0, 0, B, -100, C, 32, None) == SHAPE         # block_cols 0
+    assert f(A, 1024, 8, 1024, 0, 6, B, -100, C, 32, None) == SHAPE         # not a multiple of 4
+    assert f(A, 1024, 8, 1024, 0, 256, B, -100, C, 28, None) == SHAPE       # stride < 4 n
+    assert f(A, 1024, 8, 1024, 0, 256, B, -100, C, 34, None) == ALIGN       # stride % 4
+    assert f(A, 1024, 8, 1024, 0, 256, B, -100, C + 4, 32, None) == ALIGN   # part 16-B
+    assert f(A, 1024, 8, 1024, 0, 256, B + 2, -100, C, 32, None) == ALIGN   # target 4-B
+    assert f(A, 1026, 8, 1024, 0, 256, B, -100, C, 32, None) == ALIGN       # ld % 4
+    assert f(None, 1024, 8, 1024, 0, 256, B, -100, C, 32, None) == NULL
+    assert f(A, 1024, 8, 1024, 0, 256, None, -100, C, 32, None) == NULL
+    assert f(A, 1024, 8, 1024, 0, 256, B, -100, None, 32, None) == NULL
+    assert f(A, 1024, 8, 1024, 0, 256, B, -100, A + 4096, 32, None) == ALIAS  # part in logits
+    assert f(A, 1024, 8, 1024, 0, 256, C, -100, C, 32, None) == ALIAS       # part over target
+    # the last of 4 parts (stride 64) reaches C + 3*64*4 + 32*4: a target there aliases
+    assert f(A, 1024, 8, 1024, 0, 256, C + 3 * 64 * 4, -100, C, 64, None) == ALIAS
+    # n_blocks * n_rows beyond INT32_MAX
+    assert f(A, 2**30, 2**20, 2**30, 0, 4, B, -100, C, 4 * 2**20, None) == SHAPE
+    assert f(None, 1024, 0, 1024, 0, 256, None, -100, None, 0, None) == OK
+
+
+def test_xent_merge_validation(L):
+    f = L.lmhead_xent_merge
+    # (part, n_parts, part_stride, n_rows, target, ignore, vocab, loss, stats, stream)
+    assert f(A, 4, 32, -1, B, -100, 1000, C, D, None) == SHAPE
+    assert f(A, 0, 32, 8, B, -100, 1000, C, D, None) == SHAPE               # no parts
+    assert f(A, 4, 32, 8, B, -100, 0, C, D, None) == SHAPE                  # vocab 0
+    assert f(A, 4, 28, 8, B, -100, 1000, C, D, None) == SHAPE               # stride < 4 n
+    assert f(A, 4, 34, 8, B, -100, 1000, C, D, None) == ALIGN
+    assert f(A + 8, 4, 32, 8, B, -100, 1000, C, D, None) == ALIGN
+    assert f(A, 4, 32, 8, B, -100, 1000, C, D + 4, None) == ALIGN           # stats 16-B
+    assert f(A, 4, 32, 8, B, -100, 1000, C + 2, D, None) == ALIGN           # loss 4-B
+    assert f(None, 4, 32, 8, B, -100, 1000, C, D, None) == NULL
+    assert f(A, 4, 32, 8, None, -100, 1000, C, D, None) == NULL
+    assert f(A, 4, 32, 8, B, -100, 1000, C, None, None) == NULL
+    assert f(A, 4, 32, 8, B, -100, 1000, C, A + 256, None) == ALIAS         # stats in parts
+    assert f(A, 4, 32, 8, B, -100, 1000, A + 64, D, None) == ALIAS          # loss in parts
+    assert f(A, 4, 32, 8, B, -100, 1000, D + 16, D, None) == ALIAS          # loss over stats
+    assert f(None, 4, 32, 0, None, -100, 1000, None, None, None) == OK
 
 
 def test_xent_bwd_validation(L):

@@ -300,8 +300,108 @@ def test_xent_131k_spikes_inplace():
     torch.cuda.synchronize()
     assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
     del gb
+    del g
+    # split-vocabulary forward (32 blocks of 4096 columns) at the same size:
+    # m and X_y equal the one-pass forward bitwise, d within 1e-5 relative,
+    # and the sampled rows match the oracle
+    part = lmh.lmhead_xent_partial(z, t, block_cols=4096)
+    loss_s, st_s = lmh.lmhead_xent_merge(part, t, V)
+    torch.cuda.synchronize()
+    ss = host_f32(st_s)
+    assert np.array_equal(_bits(ss[:, 0]), _bits(sh[:, 0]))
+    assert np.array_equal(_bits(ss[:, 2]), _bits(sh[:, 2]))
+    assert np.all(np.abs(ss[:, 1] - sh[:, 1]) <= 1e-5 * sh[:, 1])
+    _check_stats(ss[rows], st_ref, "131k split")
+    del part, loss_s, st_s
     # in place over the logits (the copy keeps z for nothing else)
+    g = lmh.lmhead_xent_bwd(z, st, t, inv)
     zc = z.clone()
     lmh.lmhead_xent_bwd(zc, st, t, inv, in_place=True)
     torch.cuda.synchronize()
     assert torch.equal(zc.view(torch.int32), g.view(torch.int32))
+
+
+# ------------------------------------------------ split-vocabulary forward
+
+def _check_part(p_gpu, p_ref, what=""):
+    """m_b, X_b bit-exact; own_b exact; d_b within 1e-5 relative."""
+    p_gpu = p_gpu.reshape(p_ref.shape)
+    assert np.array_equal(_bits(p_gpu[..., 0]), _bits(p_ref[..., 0].astype(np.float32))), what + " m"
+    assert np.array_equal(_bits(p_gpu[..., 2]), _bits(p_ref[..., 2].astype(np.float32))), what + " X"
+    assert np.array_equal(p_gpu[..., 3], p_ref[..., 3].astype(np.float32)), what + " own"
+    assert np.all(np.abs(p_gpu[..., 1] - p_ref[..., 1]) <= 1e-5 * p_ref[..., 1]), what + " d"
+
+
+@pytest.mark.parametrize("n,V,bc", [(1, 1, 4), (3, 7, 4), (37, 10000, 1000), (37, 10000, 4096),
+                                    (5, 4099, 4096), (128, 32768, 4096), (600, 3000, 512),
+                                    (2, 64, 8192)])
+def test_split_partial_and_merge(n, V, bc):
+    """Per-block records against the oracle's (ragged last block, one-block
+    rows, tails of 1-3 columns, a block wider than the row, padded ld); the
+    merge against the oracle's full-row statistics and the one-pass forward;
+    the backward on the merged statistics against the oracle."""
+    inp = workloads.xent_logits(n, V, sigma=2.5, spike_frac=0.05, spike=30.0, ignore_frac=0.1,
+                                seed=n * 13 + V + bc)
+    _say(f"split n={n} V={V} bc={bc}")
+    ld = (V + 3) // 4 * 4 + 8
+    z, t = dev_f32(inp.logits, ld), dev_i32(inp.target)
+    part = lmh.lmhead_xent_partial(z, t, block_cols=bc)
+    loss, st = lmh.lmhead_xent_merge(part, t, V)
+    _, st1 = lmh.lmhead_xent_fwd(z, t)
+    dl = torch.full((1,), 0.125, device="cuda")
+    g = lmh.lmhead_xent_bwd(z, st, t, dl)
+    torch.cuda.synchronize()
+    _check_part(host_f32(part), oracle.xent_partial(inp.logits, inp.target, block_cols=bc), "part")
+    st_ref = oracle.xent_fwd(inp.logits, inp.target, -100)
+    _check_stats(host_f32(st), st_ref, "merge")
+    assert np.array_equal(_bits(host_f32(loss)), _bits(host_f32(st)[:, 3]))
+    one = host_f32(st1)
+    assert np.array_equal(_bits(host_f32(st)[:, 0]), _bits(one[:, 0]))
+    assert np.array_equal(_bits(host_f32(st)[:, 2]), _bits(one[:, 2]))
+    _check_grad(host_f32(g), oracle.xent_bwd(inp.logits, inp.target, -100, 0.125))
+
+
+def test_split_two_shards_with_offset_and_stride():
+    """Two vocabulary shards (global columns [0, 6144) and [6144, 10000)),
+    each reduced with its own col0 into one strided parts buffer, merge to
+    the oracle's full-row statistics; two runs are bit-identical."""
+    n, V, a = 45, 10000, 6144
+    inp = workloads.xent_logits(n, V, sigma=2.0, spike_frac=0.1, ignore_frac=0.1, seed=77)
+    _say("split two shards")
+    z0 = dev_f32(np.ascontiguousarray(inp.logits[:, :a]))
+    z1 = dev_f32(np.ascontiguousarray(inp.logits[:, a:]))
+    t = dev_i32(inp.target)
+    nb0, nb1 = a // 2048, -(-(V - a) // 2048)
+    buf = torch.full((nb0 + nb1, n + 3, 4), float("nan"), device="cuda")  # stride 4 (n + 3)
+    parts = buf[:, :n, :]
+    lmh.lmhead_xent_partial(z0, t, col0=0, block_cols=2048, part=parts[:nb0])
+    lmh.lmhead_xent_partial(z1, t, col0=a, block_cols=2048, part=parts[nb0:])
+    loss, st = lmh.lmhead_xent_merge(parts, t, V)
+    loss2, st2 = lmh.lmhead_xent_merge(parts, t, V)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:, n:, :]).all().item()       # padding rows never written
+    assert torch.equal(st.view(torch.int32), st2.view(torch.int32))
+    ph = host_f32(parts)
+    assert np.array_equal(ph[:, :, 3].sum(axis=0), np.where(inp.target == -100, 0, 1).astype(np.float32))
+    _check_stats(host_f32(st), oracle.xent_fwd(inp.logits, inp.target, -100), "shards")
+
+
+def test_split_merge_nan_rows():
+    """A target outside [0, vocab) or one that no supplied part owns gives
+    NaN X_y and loss (m, d finite); ignored rows give 0."""
+    V = 300
+    rng = np.random.default_rng(12)
+    zh = rng.normal(0, 1, (4, V)).astype(np.float32)
+    tgt = np.array([-100, 310, 20, 250], dtype=np.int32)
+    z, t = dev_f32(np.ascontiguousarray(zh[:, :200])), dev_i32(tgt)   # columns 200.. not supplied
+    part = lmh.lmhead_xent_partial(z, t, block_cols=64)
+    loss, st = lmh.lmhead_xent_merge(part, t, V)
+    torch.cuda.synchronize()
+    sh, lh = host_f32(st), host_f32(loss)
+    assert sh[0, 2] == 0 and lh[0] == 0
+    assert np.isnan(lh[1]) and np.isnan(sh[1, 2])
+    assert np.isfinite(lh[2]) and sh[2, 2] == zh[2, 20]
+    assert np.isnan(lh[3]) and np.isnan(sh[3, 2])
+    assert np.isfinite(sh[:, :2]).all()
+    ref = oracle.xent_merge(oracle.xent_partial(zh[:, :200], tgt, block_cols=64), tgt, V)
+    assert np.array_equal(np.isnan(ref[:, 3]), np.isnan(lh))
