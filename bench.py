@@ -358,6 +358,43 @@ def main():
             del zs, ts, ls, ss, ps
         out["xent_fwd_split_vocab"] = split
         del z
+        # Single-read forward + backward (upstream gradient known in advance)
+        # beside forward then backward, BF16 and FP32 gradients.
+        log("[bench] CE forward+backward: two reads vs one (fused)")
+        fused = {}
+        for n_s, v_s in ((128, 32768), (1024, 32768)):
+            zs = torch.randn((n_s, v_s), device="cuda", generator=gen) * 3.0
+            ts = torch.randint(0, v_s, (n_s,), device="cuda", generator=gen, dtype=torch.int32)
+            ls = torch.empty((n_s,), dtype=torch.float32, device="cuda")
+            ss = torch.empty((n_s, 4), dtype=torch.float32, device="cuda")
+            dls = torch.full((1,), 1.0 / n_s, device="cuda")
+            for gname, gdt, gsz in (("bf16", torch.bfloat16, 2), ("fp32", torch.float32, 4)):
+                gs = torch.empty((n_s, v_s), dtype=gdt, device="cuda")
+                two = lambda: (lmh.lmhead_xent_fwd(zs, ts, -100, loss=ls, stats=ss),
+                               lmh.lmhead_xent_bwd(zs, ss, ts, dls, -100, dlogits=gs,
+                                                   grad_dtype=gname))
+                one = lambda: lmh.lmhead_xent_fused(zs, ts, dls, -100, dlogits=gs,
+                                                    grad_dtype=gname, loss=ls, stats=ss)
+                for _ in range(3):
+                    two()
+                    one()
+                ftm = KernelTimer(torch)
+                for i in range(args.samples):
+                    for name, fn in ((("two", two), ("one", one)) if i % 2 == 0
+                                     else (("one", one), ("two", two))):
+                        ftm(name, fn)
+                torch.cuda.synchronize()
+                t2, t1 = statistics.median(ftm.ms("two")), statistics.median(ftm.ms("one"))
+                b2 = (8.0 + gsz) * n_s * v_s + 48 * n_s
+                b1 = (4.0 + gsz) * n_s * v_s + 24 * n_s
+                fused[f"{n_s}x{v_s}_{gname}"] = {
+                    "two_read_ms": t2, "fused_ms": t1, "speedup": t2 / t1,
+                    "two_read_gbps": b2 / (t2 * 1e-3) / 1e9, "fused_gbps": b1 / (t1 * 1e-3) / 1e9}
+                log(f"[bench]   {n_s}x{v_s} {gname}: fwd+bwd {t2 * 1e3:.1f} us, fused "
+                    f"{t1 * 1e3:.1f} us")
+                del gs
+            del zs, ts, ls, ss, dls
+        out["xent_fused_vs_two_read"] = fused
 
     # ------------------------------------------ counter calibration copy
     if args.calib_copy_mib > 0:

@@ -164,7 +164,9 @@ int32_t lmhead_xent_merge(const float *part, int64_t n_parts, int64_t part_strid
  * lmhead_xent_mean -- mean reduction of the per-row loss
  *
  *  loss     FP32 [n_rows]; target int32 [n_rows] (rows equal to ignore_index
- *           are excluded).
+ *           are excluded).  loss may be NULL when mean_out is NULL: 1 / n_valid
+ *           depends on the targets only, so it can be had before the forward
+ *           (for lmhead_xent_fused).
  *  mean_out FP32 scalar: sum of valid losses / n_valid (0 if n_valid == 0),
  *           or NULL.
  *  inv_nvalid_out FP32 scalar: 1 / n_valid (0 if n_valid == 0), or NULL; it is
@@ -206,6 +208,33 @@ int32_t lmhead_xent_bwd(const float *logits, int64_t ld, const float *stats,
                         const float *dloss, int64_t dloss_stride,
                         void *dlogits, int64_t ldg, int32_t grad_dtype,
                         int64_t n_rows, int64_t n_cols, void *stream);
+
+/*
+ * lmhead_xent_fused -- forward and backward in one read of the logits ([XENT])
+ *
+ *  For an upstream gradient known before the forward (a mean loss: dloss =
+ *  1 / n_valid, which lmhead_xent_mean gives from the targets alone): writes
+ *  the forward's loss and stats record (as lmhead_xent_fwd) and the
+ *  backward's dlogits (as lmhead_xent_bwd) while reading the logits once.
+ *  [XENT]'s discussion: the original fused kernel wrote the gradient over its
+ *  input during the forward; the FP32 backward of [XENT] "Changes" is kept.
+ *  Rows of up to 65536 columns are held in registers by one workgroup per
+ *  row (8 bytes of traffic per element with FP32 gradients instead of 12);
+ *  longer rows run the forward and then the backward (two reads).
+ *
+ *  Arguments as lmhead_xent_fwd (logits, ld, n_rows, n_cols, target,
+ *  ignore_index, loss (may be NULL), stats) and lmhead_xent_bwd (dloss,
+ *  dloss_stride, dlogits, ldg, grad_dtype, in place when dlogits == logits
+ *  with ldg == ld and LMH_FP32).  The stats, loss and dlogits outputs must not
+ *  overlap each other, the target or dloss; stats and loss must not overlap
+ *  the logits.  Results agree with lmhead_xent_fwd + lmhead_xent_bwd to
+ *  rounding (the row reduction runs over a different thread layout).
+ */
+int32_t lmhead_xent_fused(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                          const int32_t *target, int32_t ignore_index,
+                          const float *dloss, int64_t dloss_stride,
+                          float *loss, float *stats,
+                          void *dlogits, int64_t ldg, int32_t grad_dtype, void *stream);
 
 /*
  * lmhead_dgrad -- input gradient dX[M x K] = dlogits[M x V] . W[V x K]

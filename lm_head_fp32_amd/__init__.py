@@ -44,6 +44,8 @@ _SIGNATURES = {
     "lmhead_xent_partial": ([_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _vp], _i32),
     "lmhead_xent_merge": ([_vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _vp], _i32),
     "lmhead_xent_mean": ([_vp, _vp, _i32, _i64, _vp, _vp, _vp], _i32),
+    "lmhead_xent_fused": ([_vp, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _vp, _vp, _vp, _i64, _i32,
+                           _vp], _i32),
     "lmhead_xent_bwd": ([_vp, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _i64, _i32, _i64, _i64,
                          _vp], _i32),
     "lmhead_dgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
@@ -244,10 +246,19 @@ def _parts(part, n):
 
 
 def lmhead_xent_mean(loss, target, ignore_index=-100, mean=None, inv_nvalid=None, stream=None):
-    """Mean over non-ignored rows: returns (mean [1], inv_nvalid [1]) on the GPU."""
-    n = loss.numel()
-    pl = _vec(loss, "loss", torch.float32, n)
+    """Mean over non-ignored rows: returns (mean [1], inv_nvalid [1]) on the GPU.
+    loss=None computes 1/n_valid only (from the targets) and returns
+    (None, inv_nvalid)."""
+    n = target.numel()
     pt = _vec(target, "target", torch.int32, n)
+    if loss is None:
+        if inv_nvalid is None:
+            inv_nvalid = _empty((1,), torch.float32, target)
+        pi = _vec(inv_nvalid, "inv_nvalid", torch.float32, 1)
+        _check("lmhead_xent_mean", lib().lmhead_xent_mean(None, pt, int(ignore_index), n, None, pi,
+                                                          _stream(stream)))
+        return None, inv_nvalid
+    pl = _vec(loss, "loss", torch.float32, n)
     if mean is None:
         mean = _empty((1,), torch.float32, loss)
     if inv_nvalid is None:
@@ -291,6 +302,45 @@ def lmhead_xent_bwd(logits, stats, target, dloss, ignore_index=-100, dlogits=Non
     _check("lmhead_xent_bwd", lib().lmhead_xent_bwd(pz, ld, ps, pt, int(ignore_index), pd, stride,
                                                     pg, ldg, code, n, V, _stream(stream)))
     return dlogits
+
+
+def lmhead_xent_fused(logits, target, dloss, ignore_index=-100, dlogits=None, grad_dtype="fp32",
+                      in_place=False, loss=None, stats=None, stream=None):
+    """Forward and backward in one read of the logits, for an upstream
+    gradient known before the forward: returns (loss [n], stats [n, 4],
+    dlogits).  dloss as in lmhead_xent_bwd; in_place=True writes the FP32
+    gradient over `logits`."""
+    code = _dtype_code(grad_dtype)
+    pz, ld = _mat(logits, "logits", torch.float32)
+    n, V = logits.shape
+    pt = _vec(target, "target", torch.int32, n)
+    if not isinstance(dloss, torch.Tensor) or not dloss.is_cuda or dloss.dtype != torch.float32:
+        raise TypeError("dloss: expected a GPU fp32 tensor")
+    if dloss.numel() == 1:
+        stride = 0
+    elif dloss.numel() == n and dloss.is_contiguous():
+        stride = 1
+    else:
+        raise ValueError("dloss must hold 1 or n_rows contiguous values")
+    if stats is None:
+        stats = _empty((n, STATS_COLS), torch.float32, logits)
+    if loss is None:
+        loss = _empty((n,), torch.float32, logits)
+    ps = _vec(stats, "stats", torch.float32, n * STATS_COLS)
+    pl = _vec(loss, "loss", torch.float32, n) if loss is not False else None
+    if in_place:
+        dlogits = logits
+    elif dlogits is None:
+        if code not in (LMH_BF16, LMH_FP32):
+            _check("lmhead_xent_fused", 1)
+        dlogits = _empty_rows(n, V, _TORCH_DT[code], logits)
+    pg, ldg = _mat(dlogits, "dlogits", dlogits.dtype)
+    if dlogits.shape != (n, V):
+        raise ValueError("dlogits must be [n, V]")
+    _check("lmhead_xent_fused",
+           lib().lmhead_xent_fused(pz, ld, n, V, pt, int(ignore_index), _vp(dloss.data_ptr()),
+                                   stride, pl, ps, pg, ldg, code, _stream(stream)))
+    return (loss if loss is not False else None), stats, dlogits
 
 
 def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", stream=None):

@@ -226,13 +226,61 @@ int32_t lmhead_xent_mean(const float *loss, const int32_t *target, int32_t ignor
         return LMH_ERR_SHAPE;
     if (!mean_out && !inv_nvalid_out)
         return LMH_OK;
-    if (n_rows > 0 && (!loss || !target))
+    if (n_rows > 0 && (!target || (mean_out && !loss)))
         return LMH_ERR_NULL;
     if ((loss && !aligned4(loss)) || (target && !aligned4(target)) ||
         (mean_out && !aligned4(mean_out)) || (inv_nvalid_out && !aligned4(inv_nvalid_out)))
         return LMH_ERR_ALIGN;
     return launch_status(lmh::launch_xent_mean(loss, target, ignore_index, n_rows, mean_out,
                                                inv_nvalid_out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_xent_fused(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                          const int32_t *target, int32_t ignore_index, const float *dloss,
+                          int64_t dloss_stride, float *loss, float *stats, void *dlogits,
+                          int64_t ldg, int32_t grad_dtype, void *stream)
+{
+    LMH_TRY(check_dtype_out(grad_dtype));
+    if (n_rows < 0 || n_cols < 0 || n_rows > kMaxDim || n_cols > kMaxDim)
+        return LMH_ERR_SHAPE;
+    if (dloss_stride != 0 && dloss_stride != 1)
+        return LMH_ERR_SHAPE;
+    if (n_rows == 0)
+        return LMH_OK;
+    if (n_cols < 1)
+        return LMH_ERR_SHAPE;
+    const bool bf16 = grad_dtype == LMH_BF16;
+    LMH_TRY(check_matrix(logits, n_rows, n_cols, ld, 4));
+    LMH_TRY(check_matrix(dlogits, n_rows, n_cols, ldg, bf16 ? 8 : 4));
+    if (!stats || !target || !dloss)
+        return LMH_ERR_NULL;
+    if (!aligned16(stats) || !aligned4(target) || !aligned4(dloss) || (loss && !aligned4(loss)))
+        return LMH_ERR_ALIGN;
+    const Span sz = span_of(logits, n_rows, n_cols, ld, 4);
+    const Span sg = span_of(dlogits, n_rows, n_cols, ldg, bf16 ? 2 : 4);
+    const bool in_place = static_cast<const void *>(dlogits) == static_cast<const void *>(logits);
+    if (in_place) {
+        if (bf16 || ldg != ld)
+            return LMH_ERR_ALIAS;
+    } else if (overlaps(sz, sg)) {
+        return LMH_ERR_ALIAS;
+    }
+    const int64_t ndl = dloss_stride == 0 ? 1 : n_rows;
+    const Span st = span_of(target, 1, n_rows, n_rows, 4);
+    const Span sd = span_of(dloss, 1, ndl, ndl, 4);
+    const Span ss = span_of(stats, n_rows, 4, 4, 4);
+    if (overlaps(sg, ss) || overlaps(sg, st) || overlaps(sg, sd) || overlaps(ss, sz) ||
+        overlaps(ss, st) || overlaps(ss, sd))
+        return LMH_ERR_ALIAS;
+    if (loss) {
+        const Span sl = span_of(loss, 1, n_rows, n_rows, 4);
+        if (overlaps(sl, sz) || overlaps(sl, sg) || overlaps(sl, ss) || overlaps(sl, st) ||
+            overlaps(sl, sd))
+            return LMH_ERR_ALIAS;
+    }
+    return launch_status(lmh::launch_xent_fused(logits, ld, n_rows, n_cols, target, ignore_index,
+                                                dloss, dloss_stride, loss, stats, dlogits, ldg,
+                                                bf16, static_cast<hipStream_t>(stream)));
 }
 
 int32_t lmhead_xent_bwd(const float *logits, int64_t ld, const float *stats,

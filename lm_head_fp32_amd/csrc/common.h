@@ -40,6 +40,10 @@ hipError_t launch_xent_partial(const float *logits, int64_t ld, int64_t n_rows, 
 hipError_t launch_xent_merge(const float *part, int64_t n_parts, int64_t part_stride,
                              int64_t n_rows, const int32_t *target, int32_t ignore_index,
                              int64_t vocab, float *loss, float *stats, hipStream_t s);
+hipError_t launch_xent_fused(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                             const int32_t *target, int32_t ignore_index, const float *dloss,
+                             int64_t dloss_stride, float *loss, float *stats, void *dlogits,
+                             int64_t ldg, bool bf16_out, hipStream_t s);
 hipError_t launch_xent_mean(const float *loss, const int32_t *target, int32_t ignore_index,
                             int64_t n_rows, float *mean_out, float *inv_out, hipStream_t s);
 hipError_t launch_xent_bwd(const float *logits, int64_t ld, const float *stats,

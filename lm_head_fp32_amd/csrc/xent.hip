@@ -391,6 +391,132 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(const float *z, int64_t ld
     }
 }
 
+// Fused forward + backward for a known upstream gradient: one workgroup per
+// row holds the row in registers (PER float4 per thread), so the logits are
+// read once.  The row's (m, d) come from the same per-thread pairs, wave
+// butterfly and cross-wave merge as the forward; every thread then writes
+// the gradients of exactly the elements it read (in place is safe), with the
+// backward kernel's formula.  Also writes the forward's stats record and loss.
+template <int NT, int PER, bool OUTBF16>
+__global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t ld, int64_t V,
+                                                        const int32_t *__restrict__ tgt,
+                                                        int32_t ignore_index,
+                                                        const float *__restrict__ dloss,
+                                                        int64_t dloss_stride,
+                                                        float *__restrict__ loss,
+                                                        float4 *__restrict__ stats, void *g,
+                                                        int64_t ldg)
+{
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *zr = z + row * ld;
+    const float4 *z4 = reinterpret_cast<const float4 *>(zr);
+    const int64_t n4 = V >> 2;
+    const int64_t jt = 4 * n4 + tid;  // this thread's tail column (tid < 4)
+    const bool has_tail = tid < 4 && jt < V;
+
+    float4 v[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int64_t i = static_cast<int64_t>(p) * NT + tid;
+        v[p] = (i < n4) ? ld4<true>(z4 + i)
+                        : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    const float tv = has_tail ? zr[jt] : -INFINITY;
+
+    float m = tv;
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+        m = fmaxf(m, max4(v[p]));
+    float d = has_tail ? exp_shifted(tv, m) : 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            d += exp_shifted(v[p].x, m);
+            d += exp_shifted(v[p].y, m);
+            d += exp_shifted(v[p].z, m);
+            d += exp_shifted(v[p].w, m);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, 64);
+        const float d2 = __shfl_xor(d, off, 64);
+        merge_md(m, d, m2, d2);
+    }
+    constexpr int NW = NT / 64;
+    __shared__ float sm[NW], sd[NW];
+    __shared__ float row_m, row_d;
+    if ((tid & 63) == 0) {
+        sm[tid >> 6] = m;
+        sd[tid >> 6] = d;
+    }
+    __syncthreads();
+    const int32_t y = tgt[row];
+    const bool ignored = (y == ignore_index);
+    const bool bad = !ignored && (y < 0 || static_cast<int64_t>(y) >= V);
+    if (tid == 0) {
+        m = sm[0];
+        d = sd[0];
+        for (int w = 1; w < NW; ++w)
+            merge_md(m, d, sm[w], sd[w]);
+        float x, l;
+        if (ignored) {
+            x = 0.0f;
+            l = 0.0f;
+        } else if (bad) {
+            x = __int_as_float(0x7fc00000);
+            l = x;
+        } else {
+            x = zr[y];
+            l = (m - x) + logf(d);
+        }
+        stats[row] = make_float4(m, d, x, l);
+        if (loss)
+            loss[row] = l;
+        row_m = m;
+        row_d = d;
+    }
+    __syncthreads();
+    m = row_m;
+    d = row_d;
+    const float up = ignored ? 0.0f : dloss[dloss_stride * row];
+    const float coef = bad ? __int_as_float(0x7fc00000) : up / d;
+
+    auto grad = [&](float zv, int64_t j) {
+        if (ignored)
+            return 0.0f;
+        const float e = exp_shifted(zv, m);
+        return (j == static_cast<int64_t>(y)) ? fmaf(e, coef, -up) : e * coef;
+    };
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int64_t i = static_cast<int64_t>(p) * NT + tid;
+        if (i >= n4)
+            break;
+        float4 o;
+        o.x = grad(v[p].x, 4 * i);
+        o.y = grad(v[p].y, 4 * i + 1);
+        o.z = grad(v[p].z, 4 * i + 2);
+        o.w = grad(v[p].w, 4 * i + 3);
+        if constexpr (OUTBF16) {
+            uint2 w;
+            w.x = f32_to_bf16_bits(o.x) | (f32_to_bf16_bits(o.y) << 16);
+            w.y = f32_to_bf16_bits(o.z) | (f32_to_bf16_bits(o.w) << 16);
+            st2u<true>(reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g) + row * ldg) + i, w);
+        } else {
+            st4<true>(reinterpret_cast<float4 *>(static_cast<float *>(g) + row * ldg) + i, o);
+        }
+    }
+    if (has_tail) {
+        const float o = grad(tv, jt);
+        if constexpr (OUTBF16)
+            (static_cast<uint16_t *>(g) + row * ldg)[jt] = static_cast<uint16_t>(f32_to_bf16_bits(o));
+        else
+            (static_cast<float *>(g) + row * ldg)[jt] = o;
+    }
+}
+
 constexpr int kMeanThreads = 1024;
 
 __global__ __launch_bounds__(kMeanThreads) void xent_mean_kernel(const float *__restrict__ loss,
@@ -403,7 +529,8 @@ __global__ __launch_bounds__(kMeanThreads) void xent_mean_kernel(const float *__
     long long c = 0;
     for (int64_t i = tid; i < n; i += kMeanThreads) {
         if (tgt[i] != ignore_index) {
-            s += static_cast<double>(loss[i]);
+            if (loss)  // NULL: count only (1 / n_valid)
+                s += static_cast<double>(loss[i]);
             ++c;
         }
     }
@@ -499,6 +626,46 @@ hipError_t launch_xent_merge(const float *part, int64_t n_parts, int64_t part_st
                        dim3(256), 0, s, reinterpret_cast<const float4 *>(part), n_parts,
                        part_stride / 4, n_rows, target, ignore_index, vocab, loss,
                        reinterpret_cast<float4 *>(stats));
+    return hipGetLastError();
+}
+
+// Rows of at most kFusedMaxCols columns fit in the registers of one
+// 1024-thread workgroup (16 float4 per thread); longer rows take the
+// two-kernel path (forward, then backward: the logits are read twice).
+constexpr int64_t kFusedMaxCols = 65536;
+
+hipError_t launch_xent_fused(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
+                             const int32_t *target, int32_t ignore_index, const float *dloss,
+                             int64_t dloss_stride, float *loss, float *stats, void *dlogits,
+                             int64_t ldg, bool bf16_out, hipStream_t s)
+{
+    if (n_rows == 0)
+        return hipSuccess;
+    if (n_cols > kFusedMaxCols) {
+        const hipError_t e = launch_xent_fwd(logits, ld, n_rows, n_cols, target, ignore_index,
+                                             loss, stats, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_xent_bwd(logits, ld, stats, target, ignore_index, dloss, dloss_stride,
+                               dlogits, ldg, bf16_out, n_rows, n_cols, s);
+    }
+    float4 *st = reinterpret_cast<float4 *>(stats);
+    const dim3 grid(static_cast<unsigned>(n_rows)), block(1024);
+#define LMH_FUSED_LAUNCH(PER, BF)                                                               \
+    hipLaunchKernelGGL((xent_fused_kernel<1024, PER, BF>), grid, block, 0, s, logits, ld, n_cols, \
+                       target, ignore_index, dloss, dloss_stride, loss, st, dlogits, ldg)
+    if (n_cols <= 4 * 1024 * 8) {
+        if (bf16_out)
+            LMH_FUSED_LAUNCH(8, true);
+        else
+            LMH_FUSED_LAUNCH(8, false);
+    } else {
+        if (bf16_out)
+            LMH_FUSED_LAUNCH(16, true);
+        else
+            LMH_FUSED_LAUNCH(16, false);
+    }
+#undef LMH_FUSED_LAUNCH
     return hipGetLastError();
 }
 

@@ -174,6 +174,38 @@ def test_mean_validation(L):
     assert f(None, B, -100, 8, C, D, None) == NULL
     assert f(A + 2, B, -100, 8, C, D, None) == ALIGN
     assert f(A, B, -100, 8, None, None, None) == OK       # nothing requested
+    assert f(None, None, -100, 8, None, D, None) == NULL  # the target is always needed
+    # loss may be NULL only when the mean itself is not requested (1/n_valid
+    # depends on the targets alone); that call reaches a kernel, so only its
+    # rejection with a mean output is checked here
+    assert f(None, B, -100, 8, C, D, None) == NULL
+
+
+def test_xent_fused_validation(L):
+    f = L.lmhead_xent_fused
+    # (logits, ld, n, V, target, ignore, dloss, dloss_stride, loss, stats, dlogits, ldg, dtype, s)
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, A + 2**20, 1024, FP16, None) == DTYPE
+    assert f(A, 1024, -1, 1024, B, -100, C, 0, D, E, A + 2**20, 1024, FP32, None) == SHAPE
+    assert f(A, 1024, 8, 0, B, -100, C, 0, D, E, A + 2**20, 1024, FP32, None) == SHAPE
+    assert f(A, 1024, 8, 1024, B, -100, C, 2, D, E, A + 2**20, 1024, FP32, None) == SHAPE
+    assert f(A, 1000, 8, 1024, B, -100, C, 0, D, E, A + 2**20, 1024, FP32, None) == SHAPE
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, A + 2**20, 1020, FP32, None) == SHAPE
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, A + 2**20, 1028, BF16, None) == ALIGN
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E + 4, A + 2**20, 1024, FP32, None) == ALIGN
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D + 2, E, A + 2**20, 1024, FP32, None) == ALIGN
+    assert f(A, 1024, 8, 1024, None, -100, C, 0, D, E, A + 2**20, 1024, FP32, None) == NULL
+    assert f(A, 1024, 8, 1024, B, -100, None, 0, D, E, A + 2**20, 1024, FP32, None) == NULL
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, None, A + 2**20, 1024, FP32, None) == NULL
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, None, 1024, FP32, None) == NULL
+    # in place only as FP32 with the same leading dimension
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, A, 1024, BF16, None) == ALIAS
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, A + 64, 1024, FP32, None) == ALIAS
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, A + 4096, A + 2**20, 1024, FP32, None) == ALIAS
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, A, E, A + 2**20, 1024, FP32, None) == ALIAS
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, E + 16, E, A + 2**20, 1024, FP32, None) == ALIAS
+    assert f(A, 1024, 8, 1024, B, -100, C, 0, D, E, B, 1024, FP32, None) == ALIAS
+    assert f(A, 1024, 8, 1024, B, -100, A + 2**20 + 8, 0, D, E, A + 2**20, 1024, FP32, None) == ALIAS
+    assert f(None, 1024, 0, 1024, None, -100, None, 0, None, None, None, 1024, FP32, None) == OK
 
 
 def test_dgrad_wgrad_validation(L):

@@ -405,3 +405,80 @@ def test_split_merge_nan_rows():
     assert np.isfinite(sh[:, :2]).all()
     ref = oracle.xent_merge(oracle.xent_partial(zh[:, :200], tgt, block_cols=64), tgt, V)
     assert np.array_equal(np.isnan(ref[:, 3]), np.isnan(lh))
+
+
+# ------------------------------------------- single-read fused forward+backward
+
+@pytest.mark.parametrize("n,V,mode", [(1, 1, "scalar"), (3, 5, "per_row"), (33, 65, "scalar"),
+                                      (600, 4097, "per_row"), (128, 32768, "scalar"),
+                                      (5, 40001, "per_row"), (7, 65536, "scalar"),
+                                      (3, 65537, "per_row")])
+def test_fused_matches_oracle(n, V, mode):
+    """Stats and gradients of the one-read kernel against the oracle: 8 and 16
+    float4 per thread, ragged tails, ignored rows, scalar and per-row dloss,
+    rows past 65536 columns (the two-kernel path); BF16 == RNE(FP32);
+    in place == out of place bitwise; agrees with fwd + bwd to rounding."""
+    inp = workloads.xent_logits(n, V, sigma=2.5, spike_frac=0.1, spike=30.0, ignore_frac=0.15,
+                                seed=n * 7 + V)
+    _say(f"fused n={n} V={V} {mode}")
+    rng = np.random.default_rng(V)
+    if mode == "scalar":
+        dl_host = np.float32(0.0625)
+        dl = torch.full((1,), float(dl_host), device="cuda")
+        dl_ref = float(dl_host)
+    else:
+        dl_host = rng.uniform(0.1, 1.0, n).astype(np.float32)
+        dl = torch.from_numpy(dl_host).cuda()
+        dl_ref = dl_host.astype(np.float64)
+    ld = (V + 3) // 4 * 4
+    z, t = dev_f32(inp.logits, ld), dev_i32(inp.target)
+    g = padded_out(n, V, ld + 8, torch.float32)
+    loss, st, _ = lmh.lmhead_xent_fused(z, t, dl, dlogits=g)
+    _, st16, g16 = lmh.lmhead_xent_fused(z, t, dl, grad_dtype="bf16")
+    _, st2 = lmh.lmhead_xent_fwd(z, t)
+    g2 = lmh.lmhead_xent_bwd(z, st2, t, dl)
+    zc = dev_f32(inp.logits, ld)  # a second padded copy for the in-place run
+    _, _, gi = lmh.lmhead_xent_fused(zc, t, dl, in_place=True)
+    torch.cuda.synchronize()
+    st_ref = oracle.xent_fwd(inp.logits, inp.target, -100)
+    _check_stats(host_f32(st), st_ref, "fused")
+    assert np.array_equal(_bits(host_f32(loss)), _bits(host_f32(st)[:, 3]))
+    assert torch.equal(st.view(torch.int32), st16.view(torch.int32))
+    g_ref = oracle.xent_bwd(inp.logits, inp.target, -100, dl_ref)
+    _check_grad(host_f32(g), g_ref)
+    assert padding_untouched(g)
+    assert torch.equal(g16.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(gi.view(torch.int32), g.view(torch.int32))
+    assert np.array_equal(_bits(host_f32(st)[:, 0]), _bits(host_f32(st2)[:, 0]))
+    _check_grad(host_f32(g), host_f32(g2).astype(np.float64), tol=1e-6, what="fused vs fwd+bwd")
+
+
+def test_fused_mean_chain_with_targets_only_inverse():
+    """The mean-loss chain in one logits read: 1/n_valid from the targets
+    alone (no loss yet), the fused kernel with it as dloss, then the mean of
+    the losses: equal to the two-read chain's mean and inverse bitwise; the
+    all-ignored and bad-target rows behave as in the forward."""
+    n, V = 1024, 32768
+    inp = workloads.xent_logits(n, V, sigma=1.8, spike_frac=0.0, ignore_frac=0.05,
+                                seed=workloads.SEED + 9)
+    tgt = inp.target.copy()
+    tgt[3] = V + 5                                     # bad target: NaN row only
+    _say("fused mean chain")
+    z, t = dev_f32(inp.logits), dev_i32(tgt)
+    _, inv0 = lmh.lmhead_xent_mean(None, t)
+    loss, st, gb = lmh.lmhead_xent_fused(z, t, inv0, grad_dtype="bf16")
+    mean, inv = lmh.lmhead_xent_mean(loss, t)
+    loss2, st2 = lmh.lmhead_xent_fwd(z, t)
+    mean2, inv2 = lmh.lmhead_xent_mean(loss2, t)
+    torch.cuda.synchronize()
+    assert host_f32(inv0)[0] == host_f32(inv2)[0] == np.float32(1.0 / (tgt != -100).sum())
+    assert host_f32(inv)[0] == host_f32(inv0)[0]
+    lh = host_f32(loss)
+    assert np.isnan(lh[3]) and np.isnan(host_f32(mean)[0])  # a NaN loss poisons the mean
+    assert torch.isnan(gb[3].float()).all().item()
+    ok = np.ones(n, bool)
+    ok[3] = False
+    assert torch.isfinite(gb[torch.from_numpy(ok).cuda()].float()).all().item()
+    rows = np.array([0, 1, 2, 4, 500, 1023])
+    st_ref = oracle.xent_fwd(inp.logits, inp.target, -100, rows=rows)
+    _check_stats(host_f32(st)[rows], st_ref, "fused chain")
