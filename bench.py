@@ -249,6 +249,39 @@ def main():
             "fp32_overhead_pct": 100.0 * (f32 / b16 - 1.0),
         }
         del logits_b
+        # CE forward statistics from the logits GEMM's epilogue (records per
+        # 256-column block, then the merge) against logits then the one-pass
+        # forward (which reads the 128 MiB of logits once more).
+        log("[bench] logits + CE forward: separate vs records in the GEMM epilogue")
+        tgt_e = torch.from_numpy(inp.target).cuda()
+        nparts = (V + 255) // 256
+        part = torch.empty((nparts, M, 4), dtype=torch.float32, device="cuda")
+        el = torch.empty((M,), dtype=torch.float32, device="cuda")
+        es = torch.empty((M, 4), dtype=torch.float32, device="cuda")
+        sep = lambda: (lmh.lmhead_logits(x, W, out=logits, out_dtype="fp32"),
+                       lmh.lmhead_xent_fwd(logits, tgt_e, -100, loss=el, stats=es))
+        epi = lambda: (lmh.lmhead_logits_xent(x, W, tgt_e, -100, out=logits, part=part),
+                       lmh.lmhead_xent_merge(part, tgt_e, V, -100, loss=el, stats=es))
+        for _ in range(5):
+            sep()
+            epi()
+        etm = KernelTimer(torch)
+        for i in range(args.samples):
+            for name, fn in ((("sep", sep), ("epi", epi)) if i % 2 == 0 else (("epi", epi), ("sep", sep))):
+                etm(name, fn)
+            etm("gemm_stats", lambda: lmh.lmhead_logits_xent(x, W, tgt_e, -100, out=logits, part=part))
+            etm("gemm", lambda: lmh.lmhead_logits(x, W, out=logits, out_dtype="fp32"))
+        torch.cuda.synchronize()
+        tsep, tepi = statistics.median(etm.ms("sep")), statistics.median(etm.ms("epi"))
+        tgs, tg = statistics.median(etm.ms("gemm_stats")), statistics.median(etm.ms("gemm"))
+        out["logits_ce_fwd_epilogue_stats"] = {
+            "logits_then_xent_fwd_ms": tsep, "logits_with_records_then_merge_ms": tepi,
+            "saved_pct": 100.0 * (1.0 - tepi / tsep),
+            "gemm_ms": tg, "gemm_with_records_ms": tgs,
+            "epilogue_overhead_pct": 100.0 * (tgs / tg - 1.0)}
+        log(f"[bench]   separate {tsep:.3f} ms, epilogue records {tepi:.3f} ms "
+            f"(GEMM {tg:.3f} -> {tgs:.3f} ms)")
+        del part, el, es, tgt_e
         # Large-vocabulary CE
         n_ce, v_ce = args.ce_rows, 131072
         log(f"[bench] generating CE logits {n_ce}x{v_ce}")

@@ -86,6 +86,31 @@ int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw,
                       int64_t M, int64_t K, int64_t V, void *stream);
 
 /*
+ * lmhead_logits_xent -- FP32 logits plus their cross-entropy block records
+ *
+ *  The FP32 logits of lmhead_logits (out_dtype LMH_FP32) and, from the same
+ *  FP32 accumulators, the records lmhead_xent_partial would write for those
+ *  logits with block_cols = 256 and col0 = 0: for each 256-column block b of
+ *  the vocabulary and each token i, part[b * part_stride + 4 i + {0..3}] =
+ *  {m_b, d_b, X_b, own_b}.  lmhead_xent_merge (n_parts = ceil(V / 256),
+ *  vocab = V) then gives the forward's stats without reading the logits:
+ *  [XENT]'s point of removing a logits read ("Description"), carried into
+ *  the GEMM's epilogue -- an extension the pages do not describe.  For
+ *  shapes whose GEMM kernel lacks this epilogue (M <= 256, or operands too
+ *  large for 32-bit tile offsets) the records are computed from the stored
+ *  logits by a second kernel (one extra read), with the same meaning.
+ *
+ *  x, W, out as lmhead_logits (out FP32, ldo a multiple of 4).  target int32
+ *  [M], global vocabulary indices; ignore_index as in the forward.
+ *  part_stride >= 4 M and a multiple of 4; part 16-byte aligned.  out, part
+ *  and target must not overlap each other or the operands.
+ */
+int32_t lmhead_logits_xent(const void *x, int64_t ldx, const void *W, int64_t ldw,
+                           float *out, int64_t ldo, int64_t M, int64_t K, int64_t V,
+                           const int32_t *target, int32_t ignore_index,
+                           float *part, int64_t part_stride, void *stream);
+
+/*
  * lmhead_xent_fwd -- fused cross-entropy forward over FP32 logits  ([XENT])
  *
  *  logits  FP32 [n_rows x n_cols], leading dimension ld >= n_cols; read once.
@@ -143,8 +168,8 @@ int32_t lmhead_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int
  *
  *  Combines n_parts partial records per row (from one or more
  *  lmhead_xent_partial calls, at part + p * part_stride + 4 i for part p) in
- *  the order p = 0, 1, ... (a running maximum, rescaled as it grows):  m = max m_p,
- *  d = sum_p d_p exp(m_p - m),  X_y
+ *  a fixed order (64 interleaved running pairs, then a butterfly), so the
+ *  result is deterministic:  m = max m_p,  d = sum_p d_p exp(m_p - m),  X_y
  *  from the one part that owns the target,  loss = (m - X_y) + log d.
  *  Writes the same stats record and loss as lmhead_xent_fwd, so that
  *  lmhead_xent_bwd can run on the merged statistics.

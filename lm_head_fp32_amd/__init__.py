@@ -40,6 +40,8 @@ _SIGNATURES = {
     "lmhead_status_str": ([_i32], ctypes.c_char_p),
     "lmhead_version": ([], _i32),
     "lmhead_logits": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
+    "lmhead_logits_xent": ([_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64,
+                            _vp], _i32),
     "lmhead_xent_fwd": ([_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp], _i32),
     "lmhead_xent_partial": ([_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _vp], _i32),
     "lmhead_xent_merge": ([_vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _vp], _i32),
@@ -177,6 +179,31 @@ def lmhead_logits(x, W, out=None, out_dtype="fp32", stream=None):
     _check("lmhead_logits", lib().lmhead_logits(px, ldx, pw, ldw, po, ldo, code, M, K, V,
                                                 _stream(stream)))
     return out
+
+
+LOGITS_STATS_BLOCK = 256  # vocabulary columns per record of lmhead_logits_xent
+
+
+def lmhead_logits_xent(x, W, target, ignore_index=-100, out=None, part=None, stream=None):
+    """FP32 logits [M, V] and their cross-entropy records part [ceil(V/256),
+    M, 4] (as lmhead_xent_partial with block_cols=256), the records computed
+    in the GEMM's epilogue where the kernel supports it.  Returns (out, part)."""
+    px, ldx = _mat(x, "x", torch.bfloat16)
+    pw, ldw = _mat(W, "W", torch.bfloat16)
+    M, K = x.shape
+    V = W.shape[0]
+    pt = _vec(target, "target", torch.int32, M)
+    if out is None:
+        out = _empty_rows(M, V, torch.float32, x)
+    po, ldo = _mat(out, "out", torch.float32)
+    nb = max((V + LOGITS_STATS_BLOCK - 1) // LOGITS_STATS_BLOCK, 1)
+    if part is None:
+        part = torch.empty((nb, M, STATS_COLS), dtype=torch.float32, device=x.device)
+    pp, stride = _parts(part, M)
+    _check("lmhead_logits_xent", lib().lmhead_logits_xent(px, ldx, pw, ldw, po, ldo, M, K, V, pt,
+                                                          int(ignore_index), pp, stride,
+                                                          _stream(stream)))
+    return out, part
 
 
 def lmhead_xent_fwd(logits, target, ignore_index=-100, loss=None, stats=None, stream=None):

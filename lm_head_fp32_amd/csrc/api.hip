@@ -14,6 +14,10 @@ namespace {
 
 constexpr int64_t kMaxDim = static_cast<int64_t>(INT_MAX);
 
+// Vocabulary columns per cross-entropy record of lmhead_logits_xent (the
+// logits GEMM's tile height).
+constexpr int64_t kLogitsStatsBlock = 256;
+
 bool aligned16(const void *p)
 {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -131,6 +135,57 @@ int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, vo
     return launch_status(lmh::launch_gemm_logits(
         p, out_dtype == LMH_FP32 ? lmh::Epi::kStoreF32 : lmh::Epi::kStoreBF16,
         static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_logits_xent(const void *x, int64_t ldx, const void *W, int64_t ldw, float *out,
+                           int64_t ldo, int64_t M, int64_t K, int64_t V, const int32_t *target,
+                           int32_t ignore_index, float *part, int64_t part_stride, void *stream)
+{
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim)
+        return LMH_ERR_SHAPE;
+    LMH_TRY(check_matrix(out, M, V, ldo, 4));
+    if (M == 0 || V == 0)
+        return LMH_OK;
+    const int64_t nparts = (V + kLogitsStatsBlock - 1) / kLogitsStatsBlock;
+    if (part_stride < 4 * M)
+        return LMH_ERR_SHAPE;
+    if (!target || !part)
+        return LMH_ERR_NULL;
+    if (!aligned4(target) || !aligned16(part) || part_stride % 4 != 0)
+        return LMH_ERR_ALIGN;
+    const Span so = span_of(out, M, V, ldo, 4);
+    const Span st = span_of(target, 1, M, M, 4);
+    const Span sp = span_of(part, nparts, 4 * M, part_stride, 4);
+    if (overlaps(so, st) || overlaps(so, sp) || overlaps(sp, st))
+        return LMH_ERR_ALIAS;
+    if (K > 0) {
+        LMH_TRY(check_matrix(x, M, K, ldx, 8));
+        LMH_TRY(check_matrix(W, V, K, ldw, 8));
+        const Span sx = span_of(x, M, K, ldx, 2), sw = span_of(W, V, K, ldw, 2);
+        if (overlaps(so, sx) || overlaps(so, sw) || overlaps(sp, sx) || overlaps(sp, sw))
+            return LMH_ERR_ALIAS;
+    }
+    lmh::GemmProblem p;
+    p.A = static_cast<const uint16_t *>(W);
+    p.lda = ldw;
+    p.B = static_cast<const uint16_t *>(x);
+    p.ldb = ldx;
+    p.D = out;
+    p.ldd = ldo;
+    p.R = V;
+    p.C = M;
+    p.P = K;
+    p.tgt = target;
+    p.ignore_index = ignore_index;
+    p.part4 = part;
+    p.part_stride4 = part_stride / 4;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = lmh::launch_gemm_logits(p, lmh::Epi::kStoreF32Stats, hs);
+    if (e != hipSuccess || lmh::gemm_logits_stats_in_epilogue(p))
+        return launch_status(e);
+    // Kernels without the epilogue: the records from the stored logits.
+    return launch_status(lmh::launch_xent_partial(out, ldo, M, V, 0, kLogitsStatsBlock, target,
+                                                  ignore_index, part, part_stride, hs));
 }
 
 int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,

@@ -21,12 +21,23 @@ struct GemmProblem {
     void *D;
     int64_t ldd;
     int64_t R, C, P;
+    // kStoreF32Stats only (the logits GEMM, R = vocabulary, C = tokens): the
+    // tokens' targets and the per-256-row-block cross-entropy records
+    // {m, d, X_y, own} written at part4[(r0 / 256) * part_stride4 + c].
+    const int32_t *tgt = nullptr;
+    int32_t ignore_index = 0;
+    void *part4 = nullptr;
+    int64_t part_stride4 = 0;
 };
 
-enum class Epi : int { kStoreF32 = 0, kStoreBF16 = 1, kAccumF32 = 2 };
+enum class Epi : int { kStoreF32 = 0, kStoreBF16 = 1, kAccumF32 = 2, kStoreF32Stats = 3 };
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s);
+// True when launch_gemm_logits runs kStoreF32Stats in its epilogue for p
+// (the 256 x 256 eight-wave kernels); otherwise the caller computes the
+// records from the stored logits.
+bool gemm_logits_stats_in_epilogue(const GemmProblem &p);
 hipError_t launch_gemm_dgrad(const GemmProblem &p, Epi epi, hipStream_t s);
 hipError_t launch_gemm_wgrad(const GemmProblem &p, Epi epi, hipStream_t s);
 
@@ -50,6 +61,27 @@ hipError_t launch_xent_bwd(const float *logits, int64_t ld, const float *stats,
                            const int32_t *target, int32_t ignore_index, const float *dloss,
                            int64_t dloss_stride, void *dlogits, int64_t ldg, bool bf16_out,
                            int64_t n_rows, int64_t n_cols, hipStream_t s);
+
+// exp(z - m) as one hardware base-2 exponential; the same form everywhere the
+// cross-entropy statistics are computed (CE kernels, logits GEMM epilogue).
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp_shifted(float z, float m)
+{
+    return __builtin_amdgcn_exp2f((z - m) * kLog2e);
+}
+
+// Merge two partial (m, d) pairs.  A pair with m = -inf is empty.
+__device__ __forceinline__ void merge_md(float &m, float &d, float m2, float d2)
+{
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY)
+        return;  // both empty
+    const float s1 = (m == -INFINITY) ? 0.0f : exp_shifted(m, mn);
+    const float s2 = (m2 == -INFINITY) ? 0.0f : exp_shifted(m2, mn);
+    d = d * s1 + d2 * s2;
+    m = mn;
+}
 
 // FP32 -> BF16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)

@@ -605,6 +605,103 @@ __device__ __forceinline__ void store_tile(const GemmProblem &g, f32x16 (&acc)[F
     }
 }
 
+// Cross-entropy partial statistics of a finished logits tile, from the FP32
+// accumulators just stored (R = vocabulary, C = tokens; the tile covers
+// vocabulary rows [r0, r0 + WR * 32 FR) and tokens [c0, c0 + BC)).  For every
+// token the record {m, d, X_y, own} of the tile's vocabulary block: m = max,
+// d = sum exp(z - m) over the block's rows below R, X_y = the stored logit of
+// the token's target row when it lies in the block (own = 1), else 0 and 0.
+// Lane l holds rows wr*TR + 32 i + 8 q + 4 (l / 32) + e (i < FR, q, e < 4) of
+// its FC tokens; lanes l and l ^ 32 hold the two halves of the wave's rows;
+// the WR waves along the rows are combined in order through LDS.  yt[j] is
+// the target of the lane's token j (loaded before the tile's stores).  Every
+// thread of the workgroup must call this (one barrier).
+template <int FR, int FC>
+__device__ __forceinline__ void tile_targets(const GemmProblem &g, int64_t c0, int wc, int lane,
+                                             int32_t (&yt)[FC])
+{
+#pragma unroll
+    for (int j = 0; j < FC; ++j) {
+        const int64_t c = c0 + wc * FC * 32 + j * 32 + (lane & 31);
+        yt[j] = (c < g.C) ? g.tgt[c] : g.ignore_index;
+    }
+}
+
+template <int FR, int FC, int WR, int BC>
+__device__ __forceinline__ void stats_tile(const GemmProblem &g, f32x16 (&acc)[FR][FC],
+                                           const int32_t (&yt)[FC], int64_t r0, int64_t c0,
+                                           int64_t tile_r, int wr, int wc, int lane, int tid)
+{
+    constexpr int TR = FR * 32, TC = FC * 32;
+    __shared__ float4 ep[WR][BC];
+    const int64_t rw = r0 + wr * TR;  // the wave's first row
+    const int half = lane >> 5;
+    const bool interior = rw + TR <= g.R;
+#pragma unroll
+    for (int j = 0; j < FC; ++j) {
+        const int tok = wc * TC + j * 32 + (lane & 31);
+        // The target's position in this wave's rows, if it is one of this lane's.
+        const int64_t lr64 = static_cast<int64_t>(yt[j]) - rw;
+        const bool mine = yt[j] != g.ignore_index && lr64 >= 0 && lr64 < TR &&
+                          ((lr64 >> 2) & 1) == half;
+        const int lr = mine ? static_cast<int>(lr64) : -1;
+        const int ti = lr >> 5, tq = (lr >> 3) & 3, te = lr & 3;
+        float m = -INFINITY, d = 0.0f, x = 0.0f;
+        if (interior) {
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    m = fmaxf(m, acc[i][j][e]);
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    d += exp_shifted(acc[i][j][e], m);
+        } else {
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (rw + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3) < g.R)
+                        m = fmaxf(m, acc[i][j][e]);
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (rw + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3) < g.R)
+                        d += exp_shifted(acc[i][j][e], m);
+        }
+#pragma unroll
+        for (int i = 0; i < FR; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                x = (i == ti && (e >> 2) == tq && (e & 3) == te) ? acc[i][j][e] : x;
+        const float own = mine ? 1.0f : 0.0f;
+        const float m2 = __shfl_xor(m, 32, 64), d2 = __shfl_xor(d, 32, 64);
+        const float x2 = __shfl_xor(x, 32, 64), own2 = __shfl_xor(own, 32, 64);
+        merge_md(m, d, m2, d2);
+        if (lane < 32)
+            ep[wr][tok] = make_float4(m, d, mine ? x : x2, own + own2);
+    }
+    __syncthreads();
+    for (int tok = tid; tok < BC; tok += WR * (BC / TC) * 64) {
+        const int64_t c = c0 + tok;
+        if (c >= g.C)
+            continue;
+        float4 rec = ep[0][tok];
+        for (int w = 1; w < WR; ++w) {
+            const float4 q = ep[w][tok];
+            merge_md(rec.x, rec.y, q.x, q.y);
+            if (q.w != 0.0f) {
+                rec.z = q.z;
+                rec.w += q.w;
+            }
+        }
+        static_cast<float4 *>(g.part4)[tile_r * g.part_stride4 + c] = rec;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gemm_big: BR x BC tiles, WR x WC waves (two per SIMD with 8 waves), BK = 64.
 // Operands whose contraction dimension is contiguous stream into LDS by
@@ -834,7 +931,14 @@ gemm_big(GemmProblem g, TileMap tm)
             frag_load(nA, nB, 0, 0);
     }
 
-    store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + wc * TC, lane);
+    if constexpr (EPI == static_cast<int>(Epi::kStoreF32Stats) && !AT && !BT) {
+        int32_t yt[FC];
+        tile_targets<FR, FC>(g, c0, wc, lane, yt);  // in flight during the stores
+        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + wc * TC, lane);
+        stats_tile<FR, FC, WR, BC>(g, acc, yt, r0, c0, tr, wr, wc, lane, tid);
+    } else {
+        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + wc * TC, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1203,7 +1307,14 @@ gemm_pp(GemmProblem g, TileMap tm)
     if (grp == 0)
         pp_barrier();
 
-    store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + grp * TC, lane);
+    if constexpr (EPI == static_cast<int>(Epi::kStoreF32Stats)) {
+        int32_t yt[FC];
+        tile_targets<FR, FC>(g, c0, grp, lane, yt);  // in flight during the stores
+        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + grp * TC, lane);
+        stats_tile<FR, FC, WR, BC>(g, acc, yt, r0, c0, tr, wr, grp, lane, tid);
+    } else {
+        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + grp * TC, lane);
+    }
 }
 
 hipError_t launch_pp(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
@@ -1218,6 +1329,8 @@ hipError_t launch_pp(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     const dim3 grid(static_cast<unsigned>(nwg)), block(512);
     if (epi == Epi::kStoreBF16)
         hipLaunchKernelGGL((gemm_pp<1>), grid, block, 0, s, p, tm);
+    else if (epi == Epi::kStoreF32Stats)
+        hipLaunchKernelGGL((gemm_pp<3>), grid, block, 0, s, p, tm);
     else
         hipLaunchKernelGGL((gemm_pp<0>), grid, block, 0, s, p, tm);
     return hipGetLastError();
@@ -1245,6 +1358,12 @@ hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     case Epi::kAccumF32:
         hipLaunchKernelGGL((gemm_big<BR, BC, BK, WR, WC, AT, BT, 2>), grid, block, 0, s, p, tm);
         break;
+    case Epi::kStoreF32Stats:
+        if constexpr (!AT && !BT && BR == 256 && WR == 4)
+            hipLaunchKernelGGL((gemm_big<BR, BC, BK, WR, WC, AT, BT, 3>), grid, block, 0, s, p, tm);
+        else
+            return hipErrorInvalidValue;
+        break;
     }
     return hipGetLastError();
 }
@@ -1271,6 +1390,8 @@ hipError_t launch_cfg(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     case Epi::kAccumF32:
         hipLaunchKernelGGL((gemm_kernel<BR, BC, BK, WR, WC, AT, BT, 2>), grid, block, 0, s, p, tm);
         break;
+    case Epi::kStoreF32Stats:  // never routed here (see launch_gemm_logits)
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -1289,9 +1410,18 @@ static bool big_offsets_fit(const GemmProblem &p)
 #define LMH_SMALLM_CFG 0
 #endif
 
+// The many-token logits kernels (gemm_pp, gemm_big 256 x 256 with 8 waves)
+// also write the cross-entropy records in their epilogue.
+bool gemm_logits_stats_in_epilogue(const GemmProblem &p)
+{
+    return big_offsets_fit(p) && LMH_SMALLM_CFG == 0 && p.C > 256;
+}
+
 hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 {
     // R = V (vocabulary), C = M (tokens); both operands K-contiguous.
+    if (epi == Epi::kStoreF32Stats && !gemm_logits_stats_in_epilogue(p))
+        epi = Epi::kStoreF32;  // the caller derives the records from the logits
     if (!big_offsets_fit(p))
         return launch_cfg<128, 128, 2, 2, false, false>(p, epi, 8, s);
     switch (LMH_SMALLM_CFG) {  // pinned shapes for tuning builds

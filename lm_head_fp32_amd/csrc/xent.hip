@@ -28,8 +28,6 @@ namespace lmh {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte load / store of four FP32 values, optionally marked non-temporal
@@ -64,23 +62,6 @@ __device__ __forceinline__ void st2u(uint2 *p, const uint2 &v)
     } else {
         *p = v;
     }
-}
-
-__device__ __forceinline__ float exp_shifted(float z, float m)
-{
-    return __builtin_amdgcn_exp2f((z - m) * kLog2e);
-}
-
-// Merge two partial (m, d) pairs.  A pair with m = -inf is empty.
-__device__ __forceinline__ void merge_md(float &m, float &d, float m2, float d2)
-{
-    const float mn = fmaxf(m, m2);
-    if (mn == -INFINITY)
-        return;  // both empty
-    const float s1 = (m == -INFINITY) ? 0.0f : exp_shifted(m, mn);
-    const float s2 = (m2 == -INFINITY) ? 0.0f : exp_shifted(m2, mn);
-    d = d * s1 + d2 * s2;
-    m = mn;
 }
 
 __device__ __forceinline__ float max4(const float4 &v)
@@ -244,10 +225,10 @@ __global__ __launch_bounds__(NT) void xent_partial_kernel(const float *__restric
     }
 }
 
-// Split-vocabulary forward, part 2: one thread per row merges the n_parts
-// records in order p = 0, 1, ..., eight at a time (the eight loads are issued
-// before any is used): the running pair (m, d) is rescaled to each chunk's
-// new maximum, so that m = max m_p and d = sum d_p exp(m_p - m); X_y comes
+// Split-vocabulary forward, part 2: one wavefront per row.  Lane l merges
+// the records p = l, l + 64, l + 128, ... in that order into a running pair
+// (m, d) (rescaled at each new maximum); the 64 lane pairs are then merged by
+// a butterfly, so that m = max m_p and d = sum d_p exp(m_p - m); X_y comes
 // from the single owning part.  Writes the same {m, d, X_y, loss} record as
 // xent_fwd_kernel.  No owner, several owners or a target outside [0, vocab):
 // X_y = loss = NaN.
@@ -259,41 +240,35 @@ __global__ __launch_bounds__(256) void xent_merge_kernel(const float4 *__restric
                                                          float *__restrict__ loss,
                                                          float4 *__restrict__ stats)
 {
-    constexpr int C = 8;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (row >= n_rows)
-        return;
-    float m = -INFINITY, d = 0.0f, x = 0.0f;
-    int64_t owners = 0;
-    for (int64_t p0 = 0; p0 < n_parts; p0 += C) {
-        float4 q[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c)  // past the last part: an empty record
-            q[c] = (p0 + c < n_parts) ? part[(p0 + c) * part_stride4 + row]
-                                      : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
-        float cm = q[0].x;
-#pragma unroll
-        for (int c = 1; c < C; ++c)
-            cm = fmaxf(cm, q[c].x);
-        const float mn = fmaxf(m, cm);
-        float acc = d * exp_shifted(m, mn);  // first chunk: 0 * exp2(-inf) = 0
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            acc += q[c].y * exp_shifted(q[c].x, mn);
-            if (q[c].w != 0.0f) {
-                x = q[c].z;
-                ++owners;
-            }
+        return;  // whole wavefronts only: the row is uniform per wave
+    float m = -INFINITY, d = 0.0f, x = 0.0f, owners = 0.0f;
+    for (int64_t p = lane; p < n_parts; p += 64) {
+        const float4 q = part[p * part_stride4 + row];
+        merge_md(m, d, q.x, q.y);
+        if (q.w != 0.0f) {
+            x = q.z;
+            owners += q.w;
         }
-        d = acc;
-        m = mn;
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, 64), d2 = __shfl_xor(d, off, 64);
+        const float x2 = __shfl_xor(x, off, 64), o2 = __shfl_xor(owners, off, 64);
+        merge_md(m, d, m2, d2);
+        x = (owners != 0.0f) ? x : x2;
+        owners += o2;
+    }
+    if (lane != 0)
+        return;
     const int32_t y = tgt[row];
     float l;
     if (y == ignore_index) {
         x = 0.0f;
         l = 0.0f;
-    } else if (y < 0 || static_cast<int64_t>(y) >= vocab || owners != 1) {
+    } else if (y < 0 || static_cast<int64_t>(y) >= vocab || owners != 1.0f) {
         x = __int_as_float(0x7fc00000);
         l = x;
     } else {
@@ -622,7 +597,7 @@ hipError_t launch_xent_merge(const float *part, int64_t n_parts, int64_t part_st
 {
     if (n_rows == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(xent_merge_kernel, dim3(static_cast<unsigned>((n_rows + 255) / 256)),
+    hipLaunchKernelGGL(xent_merge_kernel, dim3(static_cast<unsigned>((n_rows + 3) / 4)),
                        dim3(256), 0, s, reinterpret_cast<const float4 *>(part), n_parts,
                        part_stride / 4, n_rows, target, ignore_index, vocab, loss,
                        reinterpret_cast<float4 *>(stats));

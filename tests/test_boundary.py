@@ -78,6 +78,27 @@ def test_logits_validation(L):
     assert f(None, 64, None, 64, None, 128, FP32, 16, 64, 0, None) == OK
 
 
+def test_logits_xent_validation(L):
+    f = L.lmhead_logits_xent
+    # (x, ldx, W, ldw, out, ldo, M, K, V, target, ignore, part, part_stride, stream)
+    assert f(A, 64, B, 64, C, 1024, -1, 64, 1024, D, -100, E, 4 * 300, None) == SHAPE
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, E, 4 * 299, None) == SHAPE   # stride
+    assert f(A, 64, B, 64, C, 1026, 300, 64, 1024, D, -100, E, 4 * 300, None) == ALIGN   # ldo % 4
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, E, 4 * 300 + 2, None) == ALIGN
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, E + 8, 4 * 300, None) == ALIGN
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D + 2, -100, E, 4 * 300, None) == ALIGN
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, None, -100, E, 4 * 300, None) == NULL
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, None, 4 * 300, None) == NULL
+    assert f(None, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, E, 4 * 300, None) == NULL
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, C + 4096, 4 * 300, None) == ALIAS
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, C, -100, E, 4 * 300, None) == ALIAS
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, A, 4 * 300, None) == ALIAS  # part in x
+    assert f(A, 64, B, 64, A, 1024, 300, 64, 1024, D, -100, E, 4 * 300, None) == ALIAS  # out over x
+    # last of 4 records blocks (V = 1024, stride 1200) ends at E + (3*1200 + 1200)*4
+    assert f(A, 64, B, 64, C, 1024, 300, 64, 1024, E + 4 * 3600, -100, E, 1200, None) == ALIAS
+    assert f(None, 64, None, 64, None, 1024, 0, 64, 1024, None, -100, None, 0, None) == OK
+
+
 def test_xent_fwd_validation(L):
     f = L.lmhead_xent_fwd
     assert f(A, 1024, -1, 1024, B, -100, C, D, None) == SHAPE

@@ -255,3 +255,76 @@ def test_wgrad_integer_exact_interior_tiles():
     lmh.lmhead_wgrad(dl, x, dW=dW, accumulate=True)
     torch.cuda.synchronize()
     assert np.array_equal(_f32_bits(host_f32(dW)[rows]), _f32_bits((2 * ref).astype(np.float32)))
+
+
+# ------------------------------------- logits + cross-entropy block records
+
+def _check_records(p_gpu, p_ref, what):
+    """m_b, X_b bit-exact; own_b exact; d_b within 1e-5 relative."""
+    assert np.array_equal(_f32_bits(p_gpu[..., 0]), _f32_bits(p_ref[..., 0].astype(np.float32))), what + " m"
+    assert np.array_equal(_f32_bits(p_gpu[..., 2]), _f32_bits(p_ref[..., 2].astype(np.float32))), what + " X"
+    assert np.array_equal(p_gpu[..., 3], p_ref[..., 3].astype(np.float32)), what + " own"
+    assert np.all(np.abs(p_gpu[..., 1] - p_ref[..., 1]) <= 1e-5 * p_ref[..., 1]), what + " d"
+
+
+@pytest.mark.parametrize("M,K,V", [
+    (260, 64, 1000),     # ring kernel, ragged vocabulary (last block 232 columns), 2 stages
+    (512, 256, 2048),    # ring kernel, interior tiles
+    (300, 200, 700),     # 64-wide-stage kernel (K not a multiple of 32)
+    (264, 8224, 300),    # 64-wide-stage kernel (K > 8192)
+    (100, 64, 1000),     # few tokens: records from the stored logits
+    (16, 512, 1024),
+])
+def test_logits_xent_records_integer_exact(M, K, V):
+    """Integer operands make the FP32 logits exact, so the records computed in
+    the GEMM epilogue (or from the stored logits) can be held to the oracle's
+    records of the exact logits; targets hit the first, last and ragged-block
+    columns, some rows are ignored; the merged statistics equal the oracle's
+    full-row statistics and the one-pass forward's m and X bitwise."""
+    inp = workloads.integer_gemm(M, K, V, seed=M + K + V)
+    tgt = inp.target.copy()
+    tgt[0], tgt[1], tgt[2] = 0, V - 1, ((V - 1) // 256) * 256
+    tgt[3::7] = -100
+    _say(f"logits+records M={M} K={K} V={V}")
+    x, W, t = dev_bf16(inp.x), dev_bf16(inp.W), torch.from_numpy(tgt).cuda()
+    out, part = lmh.lmhead_logits_xent(x, W, t)
+    loss, st = lmh.lmhead_xent_merge(part, t, V)
+    _, st1 = lmh.lmhead_xent_fwd(out, t)
+    torch.cuda.synchronize()
+    L, _ = oracle.logits(inp.x, inp.W)
+    z = L.astype(np.float32)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(z))
+    _check_records(host_f32(part), oracle.xent_partial(z, tgt, block_cols=256), "records")
+    ref = oracle.xent_fwd(z, tgt, -100)
+    sh, s1 = host_f32(st), host_f32(st1)
+    assert np.array_equal(_f32_bits(sh[:, 0]), _f32_bits(ref[:, 0].astype(np.float32)))
+    assert np.array_equal(_f32_bits(sh[:, 2]), _f32_bits(ref[:, 2].astype(np.float32)))
+    assert np.array_equal(_f32_bits(sh[:, 0]), _f32_bits(s1[:, 0]))
+    assert np.all(np.abs(sh[:, 1] - ref[:, 1]) <= 1e-5 * ref[:, 1])
+
+
+def test_logits_xent_records_benchmark_shape():
+    """M=1024 K=8192 V=32768 normal operands (the benchmark's launch shape):
+    the epilogue's records merged equal the one-pass forward over the stored
+    logits (m, X bitwise; d within 1e-5); sampled rows' loss against the
+    oracle within the logits' own error bound; two runs bitwise equal."""
+    inp = workloads.lmhead_1024()
+    _say("logits+records 1024x8192x32768")
+    x, W, t = dev_bf16(inp.x), dev_bf16(inp.W), torch.from_numpy(inp.target).cuda()
+    out, part = lmh.lmhead_logits_xent(x, W, t)
+    out2, part2 = lmh.lmhead_logits_xent(x, W, t)
+    loss, st = lmh.lmhead_xent_merge(part, t, 32768)
+    _, st1 = lmh.lmhead_xent_fwd(out, t)
+    torch.cuda.synchronize()
+    assert torch.equal(part.view(torch.int32), part2.view(torch.int32))
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    sh, s1 = host_f32(st), host_f32(st1)
+    assert np.array_equal(_f32_bits(sh[:, 0]), _f32_bits(s1[:, 0]))
+    assert np.array_equal(_f32_bits(sh[:, 2]), _f32_bits(s1[:, 2]))
+    assert np.all(np.abs(sh[:, 1] - s1[:, 1]) <= 1e-5 * s1[:, 1])
+    rows = np.array([0, 1, 511, 1023])
+    L, S = oracle.logits(inp.x, inp.W, rows=rows)
+    ref = oracle.xent_fwd(L.astype(np.float32), inp.target[rows], -100)
+    # loss error <= 2 x (max logit error) + FP32 rounding of the statistics
+    bound = 2e-5 * S.max(axis=1) + 1e-5 * np.abs(ref[:, 3]) + 1e-6
+    assert np.all(np.abs(host_f32(loss)[rows] - ref[:, 3]) <= bound)
