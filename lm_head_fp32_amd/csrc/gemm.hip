@@ -821,25 +821,6 @@ gemm_big(GemmProblem g, TileMap tm)
     // One steady-state stage (see the comment above the kernel).
     auto stage_fast = [&](const uint16_t *cA, const uint16_t *cB, uint16_t *nA, uint16_t *nB,
                           int64_t kt) {
-        if constexpr (!AT)
-            opA.dma(nA, (kt + 1) * BK, wave);
-        if constexpr (!BT)
-            opB.dma(nB, (kt + 1) * BK, wave);
-        frag_load(cA, cB, 1, 1);
-        mfma_rows(0, 0, FR);
-        frag_load(cA, cB, 2, 0);
-        mfma_rows(1, 0, FR);
-        frag_load(cA, cB, 3, 1);
-        mfma_rows(0, 0, FR);
-        if constexpr (AT) {
-            opA.store(nA);
-            opA.load_fast((kt + 2) * BK);
-        }
-        if constexpr (BT) {
-            opB.store(nB);
-            opB.load_fast((kt + 2) * BK);
-        }
-        mfma_rows(1, 0, FR / 2);
         constexpr int nmf = FR * FC;
         constexpr int nrd = FR + FC;
         constexpr int ndma = (AT ? 0 : OpA::NB) + (BT ? 0 : OpB::NB);
@@ -847,8 +828,9 @@ gemm_big(GemmProblem g, TileMap tm)
         constexpr int ntl = (AT ? 8 : 0) + (BT ? 8 : 0);       // their register loads
         constexpr int WPM = (ntw + nmf - 1) / nmf;             // per MFMA of k step 2
         constexpr int LPM = (ntl + nmf - 1) / nmf;
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
+        // Interleave of k step s: its MFMAs, the next step's fragment reads,
+        // the direct loads (s = 0), the transposed stores and loads (s = 2).
+        auto pattern = [&](int s) {
 #pragma unroll
             for (int m = 0; m < nmf; ++m) {
                 if (s == 0 && m < ndma)
@@ -861,10 +843,46 @@ gemm_big(GemmProblem g, TileMap tm)
                 if (s == 2 && LPM > 0 && m * LPM < ntl)
                     __builtin_amdgcn_sched_group_barrier(kSgVmemRead, LPM, 0);
             }
+        };
+        if constexpr (!AT)
+            opA.dma(nA, (kt + 1) * BK, wave);
+        if constexpr (!BT)
+            opB.dma(nB, (kt + 1) * BK, wave);
+        frag_load(cA, cB, 1, 1);
+        mfma_rows(0, 0, FR);
+        frag_load(cA, cB, 2, 0);
+        mfma_rows(1, 0, FR);
+        if constexpr (AT || BT) {
+            // A hard scheduling boundary after k step 1: the register
+            // transposes of stage kt+1 (and the wait for their loads, issued
+            // one stage earlier) stay in k step 2 instead of being hoisted
+            // to the top of the stage.
+            pattern(0);
+            pattern(1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        frag_load(cA, cB, 3, 1);
+        mfma_rows(0, 0, FR);
+        if constexpr (AT) {
+            opA.store(nA);
+            opA.load_fast((kt + 2) * BK);
+        }
+        if constexpr (BT) {
+            opB.store(nB);
+            opB.load_fast((kt + 2) * BK);
+        }
+        mfma_rows(1, 0, FR / 2);
+        if constexpr (!(AT || BT)) {
+            pattern(0);
+            pattern(1);
+        }
+        pattern(2);
         __builtin_amdgcn_sched_group_barrier(kSgMfma, nmf / 2, 0);
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // This wave's direct loads of stage kt+1 must have landed; the ntl
+        // register loads of stage kt+2 issued after them stay in flight
+        // (vector memory loads complete in issue order).
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(ntl) : "memory");
         __builtin_amdgcn_sched_barrier(0);
         frag_load(nA, nB, 0, 0);
         mfma_rows(1, FR / 2, FR);
