@@ -605,6 +605,97 @@ __device__ __forceinline__ void store_tile(const GemmProblem &g, f32x16 (&acc)[F
     }
 }
 
+// FP32 epilogue through LDS: the tile is written out 32 columns (output rows
+// c) at a time.  The waves owning those columns put their accumulators into a
+// [32][BR] FP32 staging area (the first LDS stage buffer, free once the main
+// loop is done), 16-byte chunk k of row c stored at chunk k ^ (c % 16) so that
+// both the fragment writes and the row reads below hit distinct banks; then
+// every wave reads whole rows and stores them with one 16-byte access per
+// lane, BR * 4 contiguous bytes per row (the register layout of the MFMA
+// result would store 32 bytes into each of 32 rows per instruction).
+// EPI: plain FP32 store, FP32 accumulate (D += tile) or BF16 store (each
+// value rounded to nearest-even, 8 bytes per lane).  Every thread of the
+// workgroup must call this.
+template <int FR, int FC, int WR, int WC, int BR, int BC, int EPI>
+__device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&acc)[FR][FC],
+                                               int64_t r0, int64_t c0, int wr, int wc, int lane,
+                                               int wave, void *stage)
+{
+    constexpr int TR = FR * 32, TC = FC * 32, NW = WR * WC;
+    constexpr int CH = 32;               // tile columns per chunk
+    constexpr int ROWB = BR * 4;         // bytes per staged row
+    constexpr int LPR = BR / 4;          // lanes per row (4 floats each)
+    constexpr int RPI = 64 / LPR;        // rows per wave instruction
+    static_assert(BR == 128 || BR == 256, "staging written for 128- or 256-row tiles");
+    static_assert(TR * WR == BR && TC * WC == BC && BC % CH == 0, "tile shape");
+    char *sb = static_cast<char *>(stage);
+    __syncthreads();  // every wave is done reading the main loop's stages
+#pragma unroll
+    for (int ch = 0; ch < BC / CH; ++ch) {
+        const int cw = (ch * CH) / TC;        // the wave column that owns the chunk
+        const int j = ((ch * CH) % TC) / 32;  // its fragment column block
+        if (wc == cw) {
+            const int cl = lane & 31;
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k16 = (wr * TR + i * 32 + q * 8 + (lane >> 5) * 4) >> 2;
+                    float4 v;
+                    v.x = acc[i][j][4 * q + 0];
+                    v.y = acc[i][j][4 * q + 1];
+                    v.z = acc[i][j][4 * q + 2];
+                    v.w = acc[i][j][4 * q + 3];
+                    *reinterpret_cast<float4 *>(sb + cl * ROWB + ((k16 ^ (cl & 15)) << 4)) = v;
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rr0 = 0; rr0 < CH; rr0 += NW * RPI) {
+            const int rr = rr0 + wave * RPI + lane / LPR;
+            const int k16 = lane % LPR;
+            const int64_t c = c0 + ch * CH + rr;
+            const int64_t r = r0 + 4 * k16;
+            if (rr < CH && c < g.C && r < g.R) {
+                const float4 v = *reinterpret_cast<const float4 *>(sb + rr * ROWB +
+                                                                   ((k16 ^ (rr & 15)) << 4));
+                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
+                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
+                    if (r + 4 <= g.R) {
+                        uint2 w;
+                        w.x = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
+                        w.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
+                        *reinterpret_cast<uint2 *>(out) = w;
+                    } else {
+                        const float vv[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e)
+                            out[e] = static_cast<uint16_t>(f32_to_bf16_bits(vv[e]));
+                    }
+                    continue;
+                }
+                float *out = static_cast<float *>(g.D) + c * g.ldd + r;
+                if (r + 4 <= g.R) {
+                    float4 w = v;
+                    if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
+                        const float4 o = *reinterpret_cast<const float4 *>(out);
+                        w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
+                    }
+                    *reinterpret_cast<float4 *>(out) = w;
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+                    for (int e = 0; e < 4 && r + e < g.R; ++e) {
+                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
+                            out[e] = out[e] + vv[e];
+                        else
+                            out[e] = vv[e];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Cross-entropy partial statistics of a finished logits tile, from the FP32
 // accumulators just stored (R = vocabulary, C = tokens; the tile covers
 // vocabulary rows [r0, r0 + WR * 32 FR) and tokens [c0, c0 + BC)).  For every
@@ -733,6 +824,7 @@ gemm_big(GemmProblem g, TileMap tm)
     constexpr int FR = TR / 32, FC = TC / 32;
     constexpr int NKK = BK / 16;
     static_assert(BK == 64 && NKK == 4 && FR % 2 == 0, "schedule written for BK = 64");
+    static_assert(32 * BR * 4 <= BR * BK * 2, "the FP32 epilogue stages 32 rows in sA0");
     using OpA = std::conditional_t<AT, TransOperand<BR, BK, NT>, DmaOperand<BR, BK, NW>>;
     using OpB = std::conditional_t<BT, TransOperand<BC, BK, NT>, DmaOperand<BC, BK, NW>>;
 
@@ -952,10 +1044,10 @@ gemm_big(GemmProblem g, TileMap tm)
     if constexpr (EPI == static_cast<int>(Epi::kStoreF32Stats) && !AT && !BT) {
         int32_t yt[FC];
         tile_targets<FR, FC>(g, c0, wc, lane, yt);  // in flight during the stores
-        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + wc * TC, lane);
+        store_tile_lds<FR, FC, WR, WC, BR, BC, 0>(g, acc, r0, c0, wr, wc, lane, wave, sA0);
         stats_tile<FR, FC, WR, BC>(g, acc, yt, r0, c0, tr, wr, wc, lane, tid);
     } else {
-        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + wc * TC, lane);
+        store_tile_lds<FR, FC, WR, WC, BR, BC, EPI>(g, acc, r0, c0, wr, wc, lane, wave, sA0);
     }
 }
 
@@ -1101,7 +1193,8 @@ gemm_small(GemmProblem g, TileMap tm)
         }
         compute(sA[b], sB[b]);
     }
-    store_tile<FR, FC, EPI>(g, acc, r0 + wave * 32, c0, lane);
+    store_tile_lds<FR, FC, NW, 1, BR, BC, EPI>(g, acc, r0, c0, wave, 0, lane, wave,
+                                               sA_c(std::integral_constant<int, 0>{}));
 }
 
 template <int BC, int S>
@@ -1328,10 +1421,12 @@ gemm_pp(GemmProblem g, TileMap tm)
     if constexpr (EPI == static_cast<int>(Epi::kStoreF32Stats)) {
         int32_t yt[FC];
         tile_targets<FR, FC>(g, c0, grp, lane, yt);  // in flight during the stores
-        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + grp * TC, lane);
+        store_tile_lds<FR, FC, WR, 2, BR, BC, 0>(g, acc, r0, c0, wr, grp, lane, wave,
+                                                 sA(std::integral_constant<int, 0>{}));
         stats_tile<FR, FC, WR, BC>(g, acc, yt, r0, c0, tr, wr, grp, lane, tid);
     } else {
-        store_tile<FR, FC, EPI>(g, acc, r0 + wr * TR, c0 + grp * TC, lane);
+        store_tile_lds<FR, FC, WR, 2, BR, BC, EPI>(g, acc, r0, c0, wr, grp, lane, wave,
+                                                   sA(std::integral_constant<int, 0>{}));
     }
 }
 
