@@ -9,19 +9,20 @@
 // it to BF16 for the legacy comparison (Megatron-LM "Add mixed-precision
 // (FP32) LM output logits", section "What does this PR do?").
 //
-// Orientation: tiles are computed with the matrix-core "row" dimension on R.
-// A 32x32 MFMA leaves four consecutive rows of one column in each lane, so
-// every lane stores 16 contiguous bytes of an output row with no LDS trip.
+// Orientation: tiles are computed with the matrix-core "row" dimension on R,
+// so a 32x32 MFMA leaves four consecutive output elements of one row in each
+// lane; the epilogues stage 32 output rows at a time through LDS and store
+// whole rows.
 //
-// Two kernels:
-//  * gemm_nt_big -- the logits GEMM (both operands keep P contiguous):
-//    256 x 256 tiles, 8 waves, operand stages loaded straight into LDS by
-//    buffer loads, XOR-swizzled LDS rows, software-pipelined MFMA loop (see
-//    the comments at the kernel).
-//  * gemm_kernel -- the generic form used by dgrad and wgrad, whose operands
-//    may be stored p-major: 128 x 128 tiles, register-staged double buffer,
-//    p-major operands loaded as 8x8 blocks and transposed in registers
-//    before the LDS write (LDS rows padded by 16 bytes).
+// Kernels:
+//  * gemm_pp -- the logits GEMM with many tokens and K <= 8192: 256 x 256
+//    tiles, two wave groups one phase apart over a four-stage LDS ring.
+//  * gemm_big -- 256 x 256 / 256 x 128 / 128 x 128 tiles, two LDS stages fed
+//    by direct buffer loads; the logits GEMM for longer K, and dgrad and wgrad
+//    (p-major operands read through transposing LDS loads).
+//  * gemm_small -- the logits GEMM for few tokens (W streamed once).
+//  * gemm_kernel -- the generic register-staged form, used only when an
+//    operand's byte offsets exceed the 32-bit range of buffer loads.
 // Workgroup -> tile mapping: the hardware deals consecutive workgroup ids
 // round-robin to the 8 XCDs; ids are regrouped so that the tiles one XCD runs
 // at the same time share operand strips in that XCD's L2.
@@ -370,7 +371,6 @@ __device__ __forceinline__ void lds_barrier()
 constexpr int kSgMfma = 0x8;
 constexpr int kSgVmemRead = 0x20;
 constexpr int kSgDsRead = 0x100;
-constexpr int kSgDsWrite = 0x200;
 
 // Buffer resource over one operand tile: base = the tile's first row, range
 // checking off in practice (2^31 - 1 bytes); word 3 is the raw-buffer format.
@@ -405,7 +405,6 @@ struct DmaOperand {
     static constexpr int KCH = BK / 8;
     static constexpr int ROWS_PER_KB = 1024 / (2 * BK);
     static constexpr int NB = ROWS / ROWS_PER_KB / NW;  // direct loads per wave per stage
-    static constexpr int W = 0;                           // no register transpose
     static_assert(NB * NW * ROWS_PER_KB == ROWS, "DMA split");
     __amdgpu_buffer_rsrc_t rs;
     const uint16_t *base;  // first row of the tile
@@ -458,152 +457,98 @@ struct DmaOperand {
     }
 };
 
-// An operand stored [P][rows] (rows contiguous): every thread owns one block
-// of 8 contraction rows x W tile rows, loads it (W*2 bytes per contraction
-// row), transposes it in registers and writes W 16-byte LDS chunks.
-template <int ROWS, int BK, int NT>
-struct TransOperand {
-    static constexpr int W = ROWS * BK / 8 / NT;  // tile rows per block
-    static constexpr int RG = ROWS / W;           // blocks along the rows
-    static constexpr int NB = 0;                  // no direct loads
-    static_assert(W == 2 || W == 4 || W == 8, "block width");
-    static_assert(RG * (BK / 8) == NT, "one block per thread");
-    typedef uint32_t chunk_t __attribute__((ext_vector_type(W / 2)));
-    chunk_t v[8];
-    const uint16_t *base;  // column row0 of the operand
+// An operand stored [P][rows] (rows contiguous), moved into LDS as it lies
+// in memory by direct buffer loads: stage layout [BK p-rows][ROWS] BF16, the
+// 16-byte chunk c of p-row p kept at chunk c ^ tr_swz(p).  MFMA fragments (8
+// consecutive p of one tile row per lane) come from two transposing LDS reads
+// (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte reads of lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+// So lane 4b + a of a group addresses p-row p0 + b, tile rows n0 + 4a ..
+// n0 + 4a + 3, and lane i then holds tile row n0 + i at p-rows p0 .. p0 + 3.
+// With tr_swz(p) = 4 (p % 4) the four p-rows of a group (and two groups
+// side by side) read sixteen distinct chunks: no bank conflicts.
+__device__ __forceinline__ int tr_swz(int prow)
+{
+    return (prow & 3) << 2;
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+template <int ROWS, int BK, int NW>
+struct TrOperand {
+    static constexpr int CPR = ROWS / 8;             // 16-byte chunks per p-row
+    static constexpr int PPK = 1024 / (2 * ROWS);    // p-rows per 1 KiB direct load
+    static constexpr int NB = BK / PPK / NW;         // direct loads per wave per stage
+    static_assert(ROWS == 128 || ROWS == 256, "chunk swizzle needs >= 16 chunks per p-row");
+    static_assert(NB * NW * PPK == BK, "direct-load split");
+    const uint16_t *base;  // element (p = 0, first tile row)
     int64_t ld, row0, nrows, P;
-    int pg, rg;
-    uint32_t voff;
+    uint32_t off[NB];
+    int fa0[4];  // per-lane byte offset of fragment i's first read (k step 0)
 
     __device__ __forceinline__ void init(const uint16_t *g, int64_t ld_, int64_t row0_,
-                                         int64_t nrows_, int64_t P_, int tid)
+                                         int64_t nrows_, int64_t P_, int wave, int lane,
+                                         int frow0)
     {
         ld = ld_, row0 = row0_, nrows = nrows_, P = P_;
         base = g + row0;
-        pg = tid / RG;
-        rg = tid % RG;
-        voff = static_cast<uint32_t>((static_cast<int64_t>(pg) * 8 * ld + rg * W) * 2);
-    }
-    __device__ __forceinline__ chunk_t bload(__amdgpu_buffer_rsrc_t r, int soff) const
-    {
-        if constexpr (W == 8) {
-            auto x = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
-            return *reinterpret_cast<chunk_t *>(&x);
-        } else if constexpr (W == 4) {
-            auto x = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), soff, 0);
-            return *reinterpret_cast<chunk_t *>(&x);
-        } else {
-            auto x = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), soff, 0);
-            return *reinterpret_cast<chunk_t *>(&x);
+        // Lane l of block b lands at byte 16 l: p-row PPK*b + l/CPR, LDS chunk
+        // l%CPR, which holds the tile's chunk (l%CPR) ^ tr_swz(p-row).
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int prow = (wave * NB + i) * PPK + lane / CPR;
+            const int gc = (lane % CPR) ^ tr_swz(prow);
+            off[i] = static_cast<uint32_t>((static_cast<int64_t>(prow) * ld + gc * 8) * 2);
+        }
+        // Fragment reads: lane = 16 g + 4 b + a reads p-row 8 (g / 2) + b (+ 16 kk
+        // + 4 h) at tile row frow0 + 32 i + 16 (g % 2) + 4 a.
+        const int gq = lane >> 4, b = (lane >> 2) & 3, a = lane & 3;
+        const int prow = 8 * (gq >> 1) + b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int col = frow0 + 32 * i + 16 * (gq & 1) + 4 * a;
+            fa0[i] = prow * ROWS * 2 + (((col >> 3) ^ tr_swz(prow)) << 4) + (col & 7) * 2;
         }
     }
-    // Stage wholly inside P and tile wholly inside the rows.
-    __device__ __forceinline__ void load_fast(int64_t p0)
+    __device__ __forceinline__ void dma(uint16_t *lds, int64_t p0, int wave)
     {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(base + p0 * ld);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base + p0 * ld);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = bload(r, static_cast<int>(e * ld * 2));
+        for (int i = 0; i < NB; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, LMH_LDS_PTR(lds + (wave * NB + i) * 512), 16, static_cast<int>(off[i]), 0, 0, 0);
     }
-    __device__ __forceinline__ void load_guarded(int64_t p0)
+    // Guarded register path (ragged p tail, edge tiles): zeros past P and past
+    // the last row.
+    template <int NT>
+    __device__ __forceinline__ void staged(uint16_t *lds, int64_t p0, int tid)
     {
-        const int64_t gr = row0 + rg * W;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t gp = p0 + pg * 8 + e;
-            uint16_t t[W];
-#pragma unroll
-            for (int j = 0; j < W; ++j)
-                t[j] = 0;
-            if (gp < P) {
-                const uint16_t *src = base + gp * ld + rg * W;
-#pragma unroll
-                for (int j = 0; j < W; ++j)
-                    if (gr + j < nrows)
-                        t[j] = src[j];
+        for (int idx = tid; idx < BK * CPR; idx += NT) {
+            const int prow = idx / CPR, c = idx % CPR;
+            const int64_t pp = p0 + prow, r = row0 + c * 8;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (pp < P) {
+                const uint16_t *src = base + pp * ld + c * 8;
+                if (r + 8 <= nrows)
+                    v = load16(src);
+                else if (r < nrows)
+                    v = load_partial(src, static_cast<int>(nrows - r));
             }
-#pragma unroll
-            for (int h = 0; h < W / 2; ++h)
-                v[e][h] = static_cast<uint32_t>(t[2 * h]) | (static_cast<uint32_t>(t[2 * h + 1]) << 16);
+            *reinterpret_cast<uint4 *>(&lds[prow * ROWS + ((c ^ tr_swz(prow)) * 8)]) = v;
         }
     }
-    __device__ __forceinline__ void store(uint16_t *lds) const
+    // Fragment i (tile rows frow0 + 32 i ..) of k step kk: 8 consecutive p per lane.
+    __device__ __forceinline__ bf16x8 frag(const uint16_t *lds, int i, int kk) const
     {
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const int h = j >> 1;
-            uint4 o;
-            if (j & 1) {
-                o = make_uint4(hi_pair(v[0][h], v[1][h]), hi_pair(v[2][h], v[3][h]),
-                               hi_pair(v[4][h], v[5][h]), hi_pair(v[6][h], v[7][h]));
-            } else {
-                o = make_uint4(lo_pair(v[0][h], v[1][h]), lo_pair(v[2][h], v[3][h]),
-                               lo_pair(v[4][h], v[5][h]), lo_pair(v[6][h], v[7][h]));
-            }
-            const int row = rg * W + j;
-            *reinterpret_cast<uint4 *>(&lds[row * BK + ((pg ^ lds_swz<BK>(row)) * 8)]) = o;
-        }
+        typedef __attribute__((address_space(3))) v4i16 lds_v4;
+        const char *b0 = reinterpret_cast<const char *>(lds) + fa0[i] + 16 * kk * ROWS * 2;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4 *)(b0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4 *)(b0 + 4 * ROWS * 2));
+        const v8i16 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, c);
     }
 };
-
-// Epilogue shared by the large-tile kernels: lane l, register 4q+e of a
-// 32x32 accumulator tile holds row 8q + 4(l/32) + e, column l%32, so four
-// consecutive R values per lane go out as one 16-byte (FP32) or 8-byte
-// (BF16) store; rows and columns past the edge are not stored.
-template <int FR, int FC, int EPI>
-__device__ __forceinline__ void store_tile(const GemmProblem &g, f32x16 (&acc)[FR][FC],
-                                           int64_t rbase, int64_t cbase, int lane)
-{
-#pragma unroll
-    for (int i = 0; i < FR; ++i) {
-#pragma unroll
-        for (int j = 0; j < FC; ++j) {
-            const int64_t c = cbase + j * 32 + (lane & 31);
-            if (c >= g.C)
-                continue;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t r = rbase + i * 32 + q * 8 + (lane >> 5) * 4;
-                if (r >= g.R)
-                    continue;
-                const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                const bool full = r + 4 <= g.R;
-                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
-                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
-                    if (full) {
-                        uint2 w;
-                        w.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-                        w.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-                        *reinterpret_cast<uint2 *>(out) = w;
-                    } else {
-                        const float vv[4] = {v0, v1, v2, v3};
-                        for (int e = 0; e < 4 && r + e < g.R; ++e)
-                            out[e] = static_cast<uint16_t>(f32_to_bf16_bits(vv[e]));
-                    }
-                } else {
-                    float *out = static_cast<float *>(g.D) + c * g.ldd + r;
-                    if (full) {
-                        float4 w = make_float4(v0, v1, v2, v3);
-                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
-                            const float4 o = *reinterpret_cast<const float4 *>(out);
-                            w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
-                        }
-                        *reinterpret_cast<float4 *>(out) = w;
-                    } else {
-                        const float vv[4] = {v0, v1, v2, v3};
-                        for (int e = 0; e < 4 && r + e < g.R; ++e) {
-                            if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
-                                out[e] = out[e] + vv[e];
-                            else
-                                out[e] = vv[e];
-                        }
-                    }
-                }
-            }
-        }
-    }
-}
 
 // FP32 epilogue through LDS: the tile is written out 32 columns (output rows
 // c) at a time.  The waves owning those columns put their accumulators into a
@@ -795,19 +740,20 @@ __device__ __forceinline__ void stats_tile(const GemmProblem &g, f32x16 (&acc)[F
 
 // ---------------------------------------------------------------------------
 // gemm_big: BR x BC tiles, WR x WC waves (two per SIMD with 8 waves), BK = 64.
-// Operands whose contraction dimension is contiguous stream into LDS by
-// direct buffer loads; p-major operands (dgrad's W, wgrad's x and dlogits)
-// go through registers and an 8 x W transpose.  Two LDS stages per operand
-// as separate arrays, so that the compiler can tell a direct load into one
-// stage from the fragment reads of the other (the steady loop is unrolled by
-// two to keep the stage choice compile-time).
+// Both operands stream into LDS by direct buffer loads.  An operand whose
+// contraction dimension is contiguous (the logits' x and W, dgrad's dlogits)
+// is stored k-contiguous per tile row; a p-major one (dgrad's W, wgrad's x and
+// dlogits) is stored as it lies in memory, p-rows of the tile's row range,
+// and its MFMA fragments are read with transposing LDS loads
+// (ds_read_b64_tr_b16), so no register transpose is needed.  Two LDS stages
+// per operand as separate arrays, so that the compiler can tell a direct load
+// into one stage from the fragment reads of the other (the steady loop is
+// unrolled by two to keep the stage choice compile-time).
 //
 // Steady state (interior tile, full stages), per stage kt:
 //   top:   direct loads of stage kt+1 into the other stage (spread over the
 //          first 16-wide k step, one per MFMA);
 //   k0-2:  fragment reads one k step ahead of the MFMAs;
-//   k2:    transposed operands: stage kt+1 (loaded into registers one stage
-//          earlier) is written to the other stage, then stage kt+2 is loaded;
 //   k3:    half the MFMAs, the workgroup barrier (after this wave's direct
 //          loads landed), the first fragment reads of stage kt+1, the other
 //          half of the MFMAs -- the barrier and the read latency hide behind
@@ -825,8 +771,9 @@ gemm_big(GemmProblem g, TileMap tm)
     constexpr int NKK = BK / 16;
     static_assert(BK == 64 && NKK == 4 && FR % 2 == 0, "schedule written for BK = 64");
     static_assert(32 * BR * 4 <= BR * BK * 2, "the FP32 epilogue stages 32 rows in sA0");
-    using OpA = std::conditional_t<AT, TransOperand<BR, BK, NT>, DmaOperand<BR, BK, NW>>;
-    using OpB = std::conditional_t<BT, TransOperand<BC, BK, NT>, DmaOperand<BC, BK, NW>>;
+    // p-major operands (AT / BT) are read through transposing LDS loads.
+    using OpA = std::conditional_t<AT, TrOperand<BR, BK, NW>, DmaOperand<BR, BK, NW>>;
+    using OpB = std::conditional_t<BT, TrOperand<BC, BK, NW>, DmaOperand<BC, BK, NW>>;
 
     __shared__ __attribute__((aligned(16))) uint16_t sA0[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[BR * BK];
@@ -849,11 +796,11 @@ gemm_big(GemmProblem g, TileMap tm)
     OpA opA;
     OpB opB;
     if constexpr (AT)
-        opA.init(g.A, g.lda, r0, g.R, g.P, tid);
+        opA.init(g.A, g.lda, r0, g.R, g.P, wave, lane, wr * TR);
     else
         opA.init(g.A, g.lda, r0, g.R, g.P, wave, lane);
     if constexpr (BT)
-        opB.init(g.B, g.ldb, c0, g.C, g.P, tid);
+        opB.init(g.B, g.ldb, c0, g.C, g.P, wave, lane, wc * TC);
     else
         opB.init(g.B, g.ldb, c0, g.C, g.P, wave, lane);
 
@@ -875,13 +822,21 @@ gemm_big(GemmProblem g, TileMap tm)
         const int ka0 = ((2 * kk) ^ keyA[0]) * 8, ka1 = ((2 * kk) ^ keyA[1]) * 8;
         const int kb0 = ((2 * kk) ^ keyB[0]) * 8, kb1 = ((2 * kk) ^ keyB[1]) * 8;
 #pragma unroll
-        for (int i = 0; i < FR; ++i)
-            fa[slot][i] = *reinterpret_cast<const bf16x8 *>(
-                &lA[fbA + i * 32 * BK + ((i & 1) ? ka1 : ka0)]);
+        for (int i = 0; i < FR; ++i) {
+            if constexpr (AT)
+                fa[slot][i] = opA.frag(lA, i, kk);
+            else
+                fa[slot][i] = *reinterpret_cast<const bf16x8 *>(
+                    &lA[fbA + i * 32 * BK + ((i & 1) ? ka1 : ka0)]);
+        }
 #pragma unroll
-        for (int j = 0; j < FC; ++j)
-            fb[slot][j] = *reinterpret_cast<const bf16x8 *>(
-                &lB[fbB + j * 32 * BK + ((j & 1) ? kb1 : kb0)]);
+        for (int j = 0; j < FC; ++j) {
+            if constexpr (BT)
+                fb[slot][j] = opB.frag(lB, j, kk);
+            else
+                fb[slot][j] = *reinterpret_cast<const bf16x8 *>(
+                    &lB[fbB + j * 32 * BK + ((j & 1) ? kb1 : kb0)]);
+        }
     };
 
     f32x16 acc[FR][FC];
@@ -914,15 +869,21 @@ gemm_big(GemmProblem g, TileMap tm)
     auto stage_fast = [&](const uint16_t *cA, const uint16_t *cB, uint16_t *nA, uint16_t *nB,
                           int64_t kt) {
         constexpr int nmf = FR * FC;
-        constexpr int nrd = FR + FC;
-        constexpr int ndma = (AT ? 0 : OpA::NB) + (BT ? 0 : OpB::NB);
-        constexpr int ntw = OpA::W + OpB::W;                   // LDS writes (transposed)
-        constexpr int ntl = (AT ? 8 : 0) + (BT ? 8 : 0);       // their register loads
-        constexpr int WPM = (ntw + nmf - 1) / nmf;             // per MFMA of k step 2
-        constexpr int LPM = (ntl + nmf - 1) / nmf;
-        // Interleave of k step s: its MFMAs, the next step's fragment reads,
-        // the direct loads (s = 0), the transposed stores and loads (s = 2).
-        auto pattern = [&](int s) {
+        constexpr int nrd = FR * (AT ? 2 : 1) + FC * (BT ? 2 : 1);  // LDS reads per k step
+        constexpr int ndma = OpA::NB + OpB::NB;
+        opA.dma(nA, (kt + 1) * BK, wave);
+        opB.dma(nB, (kt + 1) * BK, wave);
+        frag_load(cA, cB, 1, 1);
+        mfma_rows(0, 0, FR);
+        frag_load(cA, cB, 2, 0);
+        mfma_rows(1, 0, FR);
+        frag_load(cA, cB, 3, 1);
+        mfma_rows(0, 0, FR);
+        mfma_rows(1, 0, FR / 2);
+        // Interleave of k steps 0-2: their MFMAs, the next step's fragment
+        // reads, and (step 0) the direct loads of stage kt+1.
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
 #pragma unroll
             for (int m = 0; m < nmf; ++m) {
                 if (s == 0 && m < ndma)
@@ -930,51 +891,12 @@ gemm_big(GemmProblem g, TileMap tm)
                 __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
                 if (m < nrd)
                     __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-                if (s == 2 && WPM > 0 && m * WPM < ntw)
-                    __builtin_amdgcn_sched_group_barrier(kSgDsWrite, WPM, 0);
-                if (s == 2 && LPM > 0 && m * LPM < ntl)
-                    __builtin_amdgcn_sched_group_barrier(kSgVmemRead, LPM, 0);
             }
-        };
-        if constexpr (!AT)
-            opA.dma(nA, (kt + 1) * BK, wave);
-        if constexpr (!BT)
-            opB.dma(nB, (kt + 1) * BK, wave);
-        frag_load(cA, cB, 1, 1);
-        mfma_rows(0, 0, FR);
-        frag_load(cA, cB, 2, 0);
-        mfma_rows(1, 0, FR);
-        if constexpr (AT || BT) {
-            // A hard scheduling boundary after k step 1: the register
-            // transposes of stage kt+1 (and the wait for their loads, issued
-            // one stage earlier) stay in k step 2 instead of being hoisted
-            // to the top of the stage.
-            pattern(0);
-            pattern(1);
-            __builtin_amdgcn_sched_barrier(0);
         }
-        frag_load(cA, cB, 3, 1);
-        mfma_rows(0, 0, FR);
-        if constexpr (AT) {
-            opA.store(nA);
-            opA.load_fast((kt + 2) * BK);
-        }
-        if constexpr (BT) {
-            opB.store(nB);
-            opB.load_fast((kt + 2) * BK);
-        }
-        mfma_rows(1, 0, FR / 2);
-        if constexpr (!(AT || BT)) {
-            pattern(0);
-            pattern(1);
-        }
-        pattern(2);
         __builtin_amdgcn_sched_group_barrier(kSgMfma, nmf / 2, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // This wave's direct loads of stage kt+1 must have landed; the ntl
-        // register loads of stage kt+2 issued after them stay in flight
-        // (vector memory loads complete in issue order).
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(ntl) : "memory");
+        // This wave's direct loads of stage kt+1 have landed; then the barrier.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         frag_load(nA, nB, 0, 0);
         mfma_rows(1, FR / 2, FR);
@@ -985,24 +907,15 @@ gemm_big(GemmProblem g, TileMap tm)
     const int64_t nk = (g.P + BK - 1) / BK;
     const int64_t nfull = g.P / BK;
     int64_t kt = 0;
-    // Prologue: stage 0 into stage buffer 0; transposed operands also fetch
-    // stage 1 into registers.
+    // Prologue: stage 0 into stage buffer 0.
     if (nk > 0) {
         const bool fast0 = interior && nfull > 0;
-        const bool fast1 = interior && nfull > 1;
-        if constexpr (AT) {
-            if (fast0) opA.load_fast(0); else opA.load_guarded(0);
-            opA.store(sA0);
-            if (nk > 1) { if (fast1) opA.load_fast(BK); else opA.load_guarded(BK); }
+        if (fast0) {
+            opA.dma(sA0, 0, wave);
+            opB.dma(sB0, 0, wave);
         } else {
-            if (fast0) opA.dma(sA0, 0, wave); else opA.template staged<NT>(sA0, 0, tid);
-        }
-        if constexpr (BT) {
-            if (fast0) opB.load_fast(0); else opB.load_guarded(0);
-            opB.store(sB0);
-            if (nk > 1) { if (fast1) opB.load_fast(BK); else opB.load_guarded(BK); }
-        } else {
-            if (fast0) opB.dma(sB0, 0, wave); else opB.template staged<NT>(sB0, 0, tid);
+            opA.template staged<NT>(sA0, 0, tid);
+            opB.template staged<NT>(sB0, 0, tid);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         frag_load(sA0, sB0, 0, 0);
@@ -1013,9 +926,9 @@ gemm_big(GemmProblem g, TileMap tm)
             stage_fast(sA1, sB1, sA0, sB0, kt + 1);
         }
     }
-    // Remaining stages (all of them for an edge tile): guarded loads.  On
-    // entry, stage kt is in stage buffer kt&1 with its first fragments read,
-    // and transposed operands hold stage kt+1 in registers.
+    // Remaining stages (all of them for an edge tile): guarded register loads
+    // with zero fill.  On entry, stage kt is in stage buffer kt&1 with its
+    // first fragments read.
     for (; kt < nk; ++kt) {
         uint16_t *cA = (kt & 1) ? sA1 : sA0;
         uint16_t *cB = (kt & 1) ? sB1 : sB0;
@@ -1023,18 +936,8 @@ gemm_big(GemmProblem g, TileMap tm)
         uint16_t *nB = (kt & 1) ? sB0 : sB1;
         compute_stage(cA, cB);
         if (kt + 1 < nk) {
-            if constexpr (AT) {
-                opA.store(nA);
-                if (kt + 2 < nk) opA.load_guarded((kt + 2) * BK);
-            } else {
-                opA.template staged<NT>(nA, (kt + 1) * BK, tid);
-            }
-            if constexpr (BT) {
-                opB.store(nB);
-                if (kt + 2 < nk) opB.load_guarded((kt + 2) * BK);
-            } else {
-                opB.template staged<NT>(nB, (kt + 1) * BK, tid);
-            }
+            opA.template staged<NT>(nA, (kt + 1) * BK, tid);
+            opB.template staged<NT>(nB, (kt + 1) * BK, tid);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + 1 < nk)
@@ -1568,19 +1471,28 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 }
 
 // dgrad / wgrad tile choice (measured on MI355X at M=1024 K=8192 V=32768 and
-// M=4096 K=16384 V=131072): 256x256 tiles with 4 waves (128x128 accumulators
-// per wave, room for two transposed staging sets) whenever there are enough
-// tiles to fill the chip; otherwise dgrad's short output (M x K) is split
-// into 256x128 tiles with 8 waves, and tiny problems use 128x128.
+// M=4096 K=16384 V=131072): the logits kernel's 256x256 tile with 8 waves
+// whenever there are at least 256 such tiles; otherwise (dgrad's short M x K
+// output at M=1024) 256x128 tiles with 8 waves, and 128x128 for tiny problems.
 template <bool AT, bool BT>
 hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
 {
     if (!big_offsets_fit(p))
         return launch_cfg<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
+#ifndef LMH_BWD_CFG
+#define LMH_BWD_CFG 0
+#endif
+    switch (LMH_BWD_CFG) {  // pinned tile shapes for tuning builds
+    case 1: return launch_big<256, 256, 4, 2, AT, BT>(p, epi, 8, s);
+    case 2: return launch_big<256, 256, 2, 2, AT, BT>(p, epi, 8, s);
+    case 3: return launch_big<256, 128, 4, 2, AT, BT>(p, epi, 8, s);
+    case 4: return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
+    default: break;
+    }
     const int64_t tiles256 = ((p.R + 255) / 256) * ((p.C + 255) / 256);
     const int64_t tiles256x128 = ((p.R + 255) / 256) * ((p.C + 127) / 128);
-    if (tiles256 >= 512 || (BT && tiles256 >= 256))
-        return launch_big<256, 256, 2, 2, AT, BT>(p, epi, 8, s);
+    if (tiles256 >= 256)
+        return launch_big<256, 256, 4, 2, AT, BT>(p, epi, 8, s);
     if (tiles256x128 >= 192)
         return launch_big<256, 128, 4, 2, AT, BT>(p, epi, 8, s);
     return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
