@@ -21,6 +21,13 @@ half of the metric.  Beside the step the same run measures:
   (N(0, 3^2), 1% rows +30 spikes, 2% ignored) -- the second half of the
   metric, in GB/s of algorithmic bytes -- out of place, in place and with
   BF16 gradients;
+* the pages' GEMM grid (M in 16/128/1024, K in 1024..16384, V = 32768),
+  FP32-out vs BF16-out with the same protocol, each shape's roofline
+  fraction, and the median FP32-output overhead;
+* the logits GEMM cold (L2 and MALL flushed between samples) and warm at
+  M=128 K=4096 and M=1024 K=8192;
+* what the chip sustains: a register-only MFMA loop and a 1 GiB copy; and
+  the vendor BLAS on the step's GEMM (BF16 out), for context;
 * the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -85,6 +92,8 @@ def parse():
     ap.add_argument("--ce-rows", type=int, default=8192, help="rows of the large CE workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the side measurements")
+    ap.add_argument("--no-grid", action="store_true",
+                    help="skip the GEMM grid, cold/warm, sustained-peak and vendor measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -108,6 +117,171 @@ class KernelTimer:
 
     def ms(self, name):
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
+
+def quantiles(ts):
+    """median, p10, p90 of a list of times."""
+    s = sorted(ts)
+    q = lambda p: s[min(len(s) - 1, max(0, int(round(p * (len(s) - 1)))))]
+    return statistics.median(s), q(0.1), q(0.9)
+
+
+def alternate(torch, samples, fns):
+    """The pages' protocol for two variants: (10 warmup pairs done by the
+    caller), then `samples` rounds in alternating order; HIP events per call."""
+    tm = KernelTimer(torch)
+    names = list(fns)
+    for i in range(samples):
+        for name in (names if i % 2 == 0 else names[::-1]):
+            tm(name, fns[name])
+    torch.cuda.synchronize()
+    return tm
+
+
+# The pages' GEMM grid: M x K at V = 32768 (Megatron-LM "Add mixed-precision
+# (FP32) LM output logits", section "GEMM kernel benchmark").
+GRID_M = (16, 128, 1024)
+GRID_K = (1024, 2048, 4096, 8192, 16384)
+GRID_V = 32768
+
+
+def gemm_grid(torch, lmh, samples, seed):
+    """FP32-out vs BF16-out logits GEMM over the 15 grid shapes (x ~ N(0,1),
+    W ~ N(0, 0.02^2) from torch's device generator), with each shape's
+    roofline fraction t_roof / t, t_roof = max(FLOP / MFMA peak, bytes / HBM
+    peak) over the compulsory bytes."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    rows = []
+    V = GRID_V
+    for K in GRID_K:
+        W = (torch.randn(V, K, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+        for M in GRID_M:
+            x = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+            o32 = torch.empty((M, V), dtype=torch.float32, device="cuda")
+            o16 = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+            fns = {"fp32": lambda: lmh.lmhead_logits(x, W, out=o32, out_dtype="fp32"),
+                   "bf16": lambda: lmh.lmhead_logits(x, W, out=o16, out_dtype="bf16")}
+            for _ in range(10):
+                fns["fp32"]()
+                fns["bf16"]()
+            tm = alternate(torch, samples, fns)
+            flop = 2.0 * M * K * V
+            r = {"M": M, "K": K, "V": V}
+            for name, osz in (("fp32", 4), ("bf16", 2)):
+                med, p10, p90 = quantiles(tm.ms(name))
+                nbytes = 2.0 * M * K + 2.0 * V * K + osz * M * V
+                t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+                t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+                r.update({f"{name}_ms": med, f"{name}_p10_ms": p10, f"{name}_p90_ms": p90,
+                          f"{name}_tflops": flop / (med * 1e-3) / 1e12,
+                          f"{name}_gbps": nbytes / (med * 1e-3) / 1e9,
+                          f"{name}_bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                          f"{name}_roofline_frac": max(t_mfma, t_hbm) / (med * 1e-3)})
+            r["fp32_overhead_pct"] = 100.0 * (r["fp32_ms"] / r["bf16_ms"] - 1.0)
+            rows.append(r)
+            log(f"[bench]   grid M={M} K={K}: fp32 {r['fp32_ms'] * 1e3:.1f} us "
+                f"({r['fp32_roofline_frac'] * 100:.0f} % of {r['fp32_bound']} roofline), "
+                f"bf16 {r['bf16_ms'] * 1e3:.1f} us, overhead {r['fp32_overhead_pct']:+.1f} %")
+            del x, o32, o16
+        del W
+    ov = [r["fp32_overhead_pct"] for r in rows]
+    ovk = [r["fp32_overhead_pct"] for r in rows if r["K"] >= 8192]
+    return {"protocol": "10 warmup pairs, then alternating fp32/bf16 samples; medians, p10/p90",
+            "shapes": rows,
+            "median_fp32_overhead_pct": statistics.median(ov),
+            "median_fp32_overhead_pct_k_ge_8192": statistics.median(ovk),
+            "pages_context": {"hardware": "NVIDIA GB300 (another machine; context, not the target)",
+                              "median_fp32_overhead_pct": 5.4,
+                              "median_fp32_overhead_pct_k_ge_8192": 1.9}}
+
+
+def cold_vs_warm(torch, lmh, samples, seed):
+    """FP32-out logits GEMM at M=128 K=4096 and M=1024 K=8192 (V=32768), warm
+    (back to back) and cold (a 512 MiB device write between samples, outside
+    the timed events, evicts the operands from L2 and the 256 MB MALL)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 1)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    res = {}
+    for M, K in ((128, 4096), (1024, 8192)):
+        V = GRID_V
+        W = (torch.randn(V, K, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+        x = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+        o = torch.empty((M, V), dtype=torch.float32, device="cuda")
+        f = lambda: lmh.lmhead_logits(x, W, out=o, out_dtype="fp32")
+        for _ in range(10):
+            f()
+        tm = KernelTimer(torch)
+        for i in range(samples):
+            tm("warm", f)
+        for i in range(samples):
+            flush.fill_(i & 0xFF)
+            tm("cold", f)
+        torch.cuda.synchronize()
+        w, wp10, wp90 = quantiles(tm.ms("warm"))
+        c, cp10, cp90 = quantiles(tm.ms("cold"))
+        flop = 2.0 * M * K * V
+        res[f"{M}x{K}x{V}"] = {"warm_ms": w, "warm_p10_ms": wp10, "warm_p90_ms": wp90,
+                               "cold_ms": c, "cold_p10_ms": cp10, "cold_p90_ms": cp90,
+                               "warm_tflops": flop / (w * 1e-3) / 1e12,
+                               "cold_tflops": flop / (c * 1e-3) / 1e12}
+        log(f"[bench]   {M}x{K}x{V}: warm {w * 1e3:.1f} us, cold {c * 1e3:.1f} us")
+        del W, x, o
+    del flush
+    return res
+
+
+def sustained_peaks(torch, lmh):
+    """What the chip sustains: a register-only MFMA loop (the library's
+    diagnostic kernel, two waves per SIMD) and a 1 GiB device copy."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_wg, iters = 2 * cus, 20000
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        lmh.lmhead_diag_mfma_loop(iters, n_wg, sink)
+    tm = KernelTimer(torch)
+    for _ in range(5):
+        tm("mfma", lambda: lmh.lmhead_diag_mfma_loop(iters, n_wg, sink))
+    torch.cuda.synchronize()
+    if not torch.all(sink == 128.0 * iters).item():
+        raise RuntimeError("MFMA loop diagnostic returned a wrong closed-form value")
+    t_mfma = statistics.median(tm.ms("mfma"))
+    mfma_tflops = n_wg * lmh.MFMA_LOOP_FLOP_PER_WORKGROUP_ITER * iters / (t_mfma * 1e-3) / 1e12
+    nb = 1 << 30
+    src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    for _ in range(10):
+        tm("copy", lambda: dst.copy_(src))
+    torch.cuda.synchronize()
+    t_copy = statistics.median(tm.ms("copy"))
+    del src, dst, sink
+    return {"mfma_bf16_loop_tflops": mfma_tflops,
+            "mfma_bf16_loop_frac_of_peak": mfma_tflops / PEAK_BF16_TFLOPS,
+            "mfma_loop": f"{n_wg} workgroups x 4 waves x 8 chains x {iters} 32x32x16 MFMAs, "
+                         "register operands only",
+            "copy_gbps": 2.0 * nb / (t_copy * 1e-3) / 1e9,
+            "copy_frac_of_peak": 2.0 * nb / (t_copy * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "copy": "1 GiB device-to-device copy, read + write bytes"}
+
+
+def vendor_context(torch, x, W, M, K, V, samples):
+    """The vendor BLAS (torch.mm -> hipBLASLt) on the step's shape with a
+    BF16 output, for context only: it is not part of the path."""
+    y = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        torch.mm(x, W.t(), out=y)
+    tm = KernelTimer(torch)
+    for _ in range(samples):
+        tm("mm", lambda: torch.mm(x, W.t(), out=y))
+    torch.cuda.synchronize()
+    med, p10, p90 = quantiles(tm.ms("mm"))
+    del y
+    return {"what": "torch.mm (hipBLASLt), BF16 x BF16 -> BF16 out, same x and W as the step",
+            "ms_median": med, "p10_ms": p10, "p90_ms": p90,
+            "tflops": 2.0 * M * K * V / (med * 1e-3) / 1e12}
 
 
 def dev_bf16(torch, np, bits):
@@ -428,6 +602,23 @@ def main():
                 del gs
             del zs, ts, ls, ss, dls
         out["xent_fused_vs_two_read"] = fused
+
+    # ------------------------- the pages' GEMM grid, cold/warm, sustained peaks
+    if not args.no_side and not args.no_grid:
+        log("[bench] the pages' GEMM grid (M x K at V=32768), fp32-out vs bf16-out")
+        out["gemm_grid_fp32_vs_bf16"] = gemm_grid(torch, lmh, args.samples, workloads.SEED)
+        g = out["gemm_grid_fp32_vs_bf16"]
+        log(f"[bench]   median fp32-out overhead {g['median_fp32_overhead_pct']:+.2f} % "
+            f"(K >= 8192: {g['median_fp32_overhead_pct_k_ge_8192']:+.2f} %)")
+        log("[bench] logits GEMM cold vs warm")
+        out["logits_cold_vs_warm"] = cold_vs_warm(torch, lmh, args.samples, workloads.SEED)
+        log("[bench] sustained peaks: MFMA loop, device copy")
+        out["sustained_peaks"] = sustained_peaks(torch, lmh)
+        sp = out["sustained_peaks"]
+        log(f"[bench]   MFMA loop {sp['mfma_bf16_loop_tflops']:.0f} TFLOPS, copy "
+            f"{sp['copy_gbps']:.0f} GB/s")
+        out["vendor_gemm_context"] = vendor_context(torch, x, W, M, K, V, args.samples)
+        log(f"[bench]   vendor BLAS (bf16 out) {out['vendor_gemm_context']['tflops']:.0f} TFLOPS")
 
     # ------------------------------------------ counter calibration copy
     if args.calib_copy_mib > 0:

@@ -287,6 +287,23 @@ int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ld
                      float *dW, int64_t ldw, int32_t accumulate,
                      int64_t M, int64_t K, int64_t V, void *stream);
 
+/*
+ * lmhead_diag_mfma_loop -- diagnostic: the sustained BF16 matrix-core rate.
+ *
+ *  Not a step of the method: a register-only loop that the benchmark runs
+ *  beside the GEMMs so their throughput can be compared with what the chip
+ *  sustains under full matrix load at its power limit (the datasheet peak
+ *  assumes 2.4 GHz).  n_workgroups workgroups of 256 threads (4 waves) each
+ *  run 8 independent chains of `iters` 32x32x16 BF16 MFMAs with all operands
+ *  1.0: 2 * 32 * 32 * 16 * 8 * iters FLOP per wave, 4 waves per workgroup.
+ *  sink FP32 [n_workgroups * 256] receives, per thread, 128 * iters exactly
+ *  (the sum of element 0 of its 8 accumulators), which checks that every
+ *  MFMA ran.  Limits: 0 <= iters, 128 * iters < 2^24 (exact in FP32) and
+ *  0 <= n_workgroups <= 65536, else LMH_ERR_SHAPE; n_workgroups == 0 is a
+ *  no-op.  sink must not be NULL (LMH_ERR_NULL) and 16-byte aligned.
+ */
+int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ __all__ = [
     "LMH_BF16", "LMH_FP32", "LMH_FP16", "STATS_COLS", "LmheadError", "lib", "library_path",
     "lmhead_logits", "lmhead_xent_fwd", "lmhead_xent_mean", "lmhead_xent_bwd",
     "lmhead_dgrad", "lmhead_wgrad", "lmhead_status_str", "lmhead_version",
+    "lmhead_diag_mfma_loop",
 ]
 
 LMH_BF16, LMH_FP32, LMH_FP16 = 0, 1, 2
@@ -52,6 +53,7 @@ _SIGNATURES = {
                          _vp], _i32),
     "lmhead_dgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
     "lmhead_wgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
+    "lmhead_diag_mfma_loop": ([_i64, _i64, _vp, _vp], _i32),
 }
 
 
@@ -409,3 +411,19 @@ def lmhead_wgrad(dlogits, x, dW=None, accumulate=False, stream=None):
     _check("lmhead_wgrad", lib().lmhead_wgrad(pd, ldd, px, ldx, pw, ldw, int(bool(accumulate)),
                                               M, K, V, _stream(stream)))
     return dW
+
+
+MFMA_LOOP_FLOP_PER_WORKGROUP_ITER = 2 * 32 * 32 * 16 * 8 * 4  # 8 chains x 4 waves
+
+
+def lmhead_diag_mfma_loop(iters, n_workgroups, sink=None, stream=None):
+    """Diagnostic register-only MFMA loop; returns sink [n_workgroups * 256]
+    FP32, every element 128 * iters when every MFMA ran."""
+    iters, n_workgroups = int(iters), int(n_workgroups)
+    if sink is None:
+        sink = torch.empty(max(n_workgroups, 0) * 256, dtype=torch.float32, device="cuda")
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < n_workgroups * 256:
+        raise ValueError("sink must be a contiguous fp32 tensor of n_workgroups * 256 elements")
+    _check("lmhead_diag_mfma_loop", lib().lmhead_diag_mfma_loop(iters, n_workgroups,
+                                                                sink.data_ptr(), _stream(stream)))
+    return sink

@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblmhead.so")
-SOURCES = ("api.hip", "gemm.hip", "xent.hip")
+SOURCES = ("api.hip", "gemm.hip", "xent.hip", "diag.hip")
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

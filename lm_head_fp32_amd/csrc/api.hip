@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = static_cast<int64_t>(INT_MAX);
+constexpr int64_t kMaxDiagWorkgroups = 65536;
 
 // Vocabulary columns per cross-entropy record of lmhead_logits_xent (the
 // logits GEMM's tile height).
@@ -101,7 +102,7 @@ const char *lmhead_status_str(int32_t status)
 
 int32_t lmhead_version(void)
 {
-    return 101;
+    return 102;
 }
 
 int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, void *out,
@@ -441,6 +442,22 @@ int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ld
     return launch_status(lmh::launch_gemm_wgrad(
         p, accumulate ? lmh::Epi::kAccumF32 : lmh::Epi::kStoreF32,
         static_cast<hipStream_t>(stream)));
+}
+
+int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, float *sink, void *stream)
+{
+    const int64_t chains = lmh::mfma_loop_chains();
+    if (iters < 0 || n_workgroups < 0 || n_workgroups > kMaxDiagWorkgroups ||
+        16 * chains * iters >= (int64_t{1} << 24))
+        return LMH_ERR_SHAPE;
+    if (n_workgroups == 0)
+        return LMH_OK;
+    if (!sink)
+        return LMH_ERR_NULL;
+    if (!aligned16(sink))
+        return LMH_ERR_ALIGN;
+    return launch_status(lmh::launch_mfma_loop(iters, n_workgroups, sink,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert lmh.lmhead_version() == 101
+    assert lmh.lmhead_version() == 102
     assert lmh.lmhead_status_str(0) == "LMH_OK"
     for s in range(1, 7):
         assert lmh.lmhead_status_str(s).startswith("LMH_ERR_")
@@ -243,6 +243,17 @@ def test_dgrad_wgrad_validation(L):
     assert w(A, 128, B, 64, B, 64, 0, 16, 64, 128, None) == ALIAS
     assert w(None, 128, B, 64, C, 64, 0, 16, 64, 128, None) == NULL
     assert w(None, 128, None, 64, C, 64, 1, 0, 64, 128, None) == OK     # M = 0, accumulate
+
+
+def test_diag_mfma_loop_validation(L):
+    f = L.lmhead_diag_mfma_loop
+    assert f(-1, 4, A, None) == SHAPE
+    assert f(1 << 17, 4, A, None) == SHAPE           # 128 * iters must stay below 2^24
+    assert f(10, -1, A, None) == SHAPE
+    assert f(10, 65537, A, None) == SHAPE
+    assert f(10, 4, None, None) == NULL
+    assert f(10, 4, A + 4, None) == ALIGN
+    assert f(10, 0, None, None) == OK                # no workgroups: no-op
 
 
 def test_binding_rejects_cpu_tensors():
