@@ -36,6 +36,8 @@ namespace lmh {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
@@ -559,8 +561,8 @@ struct TrOperand {
 // lane, BR * 4 contiguous bytes per row (the register layout of the MFMA
 // result would store 32 bytes into each of 32 rows per instruction).
 // EPI: plain FP32 store, FP32 accumulate (D += tile) or BF16 store (each
-// value rounded to nearest-even, 8 bytes per lane).  Every thread of the
-// workgroup must call this.
+// value rounded to nearest-even in registers, a [32][BR] BF16 staging area,
+// 16 bytes per lane).  Every thread of the workgroup must call this.
 template <int FR, int FC, int WR, int WC, int BR, int BC, int EPI>
 __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&acc)[FR][FC],
                                                int64_t r0, int64_t c0, int wr, int wc, int lane,
@@ -575,6 +577,58 @@ __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&ac
     static_assert(TR * WR == BR && TC * WC == BC && BC % CH == 0, "tile shape");
     char *sb = static_cast<char *>(stage);
     __syncthreads();  // every wave is done reading the main loop's stages
+    if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
+        // BF16: round in registers (v_cvt_pk_bf16_f32, nearest-even), stage
+        // BR * 2 bytes per row, the 8-byte half h of 16-byte chunk k of row c
+        // at chunk k ^ (c % 16); then 16 bytes (8 values) per lane per store.
+        constexpr int ROWB16 = BR * 2;
+        constexpr int LPR16 = BR / 8;      // lanes per row
+        constexpr int RPI16 = 64 / LPR16;  // rows per wave instruction
+#pragma unroll
+        for (int ch = 0; ch < BC / CH; ++ch) {
+            const int cw = (ch * CH) / TC;
+            const int j = ((ch * CH) % TC) / 32;
+            if (wc == cw) {
+                const int cl = lane & 31;
+#pragma unroll
+                for (int i = 0; i < FR; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int rl = wr * TR + i * 32 + q * 8 + (lane >> 5) * 4;
+                        const f32x2 lo = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]};
+                        const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        uint2 w;
+                        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+                        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+                        *reinterpret_cast<uint2 *>(sb + cl * ROWB16 +
+                                                   (((rl >> 3) ^ (cl & 15)) << 4) +
+                                                   ((rl >> 2) & 1) * 8) = w;
+                    }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int rr0 = 0; rr0 < CH; rr0 += NW * RPI16) {
+                const int rr = rr0 + wave * RPI16 + lane / LPR16;
+                const int k = lane % LPR16;
+                const int64_t c = c0 + ch * CH + rr;
+                const int64_t r = r0 + 8 * k;
+                if (rr < CH && c < g.C && r < g.R) {
+                    const uint4 v =
+                        *reinterpret_cast<const uint4 *>(sb + rr * ROWB16 + ((k ^ (rr & 15)) << 4));
+                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
+                    if (r + 8 <= g.R) {
+                        *reinterpret_cast<uint4 *>(out) = v;
+                    } else {
+                        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 8 && r + e < g.R; ++e)
+                            out[e] = static_cast<uint16_t>(vv[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
 #pragma unroll
     for (int ch = 0; ch < BC / CH; ++ch) {
         const int cw = (ch * CH) / TC;        // the wave column that owns the chunk
@@ -604,20 +658,6 @@ __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&ac
             if (rr < CH && c < g.C && r < g.R) {
                 const float4 v = *reinterpret_cast<const float4 *>(sb + rr * ROWB +
                                                                    ((k16 ^ (rr & 15)) << 4));
-                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
-                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
-                    if (r + 4 <= g.R) {
-                        uint2 w;
-                        w.x = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
-                        w.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
-                        *reinterpret_cast<uint2 *>(out) = w;
-                    } else {
-                        const float vv[4] = {v.x, v.y, v.z, v.w};
-                        for (int e = 0; e < 4 && r + e < g.R; ++e)
-                            out[e] = static_cast<uint16_t>(f32_to_bf16_bits(vv[e]));
-                    }
-                    continue;
-                }
                 float *out = static_cast<float *>(g.D) + c * g.ldd + r;
                 if (r + 4 <= g.R) {
                     float4 w = v;

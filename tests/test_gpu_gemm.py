@@ -129,18 +129,24 @@ def test_logits_lmhead_128_random_full():
     gb = oracle.bf16_bits_to_f64(host_bits(outb))
     half_ulp = np.abs(L) * 2.0 ** -8
     assert np.all(np.abs(gb - L) <= 1e-5 * S + half_ulp + 1e-30)
+    # same accumulation, rounded once: BF16 output = RNE of the FP32 output
+    # (torch's CPU conversion, nearest-even)
+    assert torch.equal(outb.cpu().view(torch.int16), out.cpu().to(torch.bfloat16).view(torch.int16))
 
 
 def test_logits_lmhead_1024_random_sampled():
     """M=1024, K=8192, V=32768 (the benchmark's launch shape): 24 sampled
-    rows x all V columns within 1e-5 * S; run twice, bitwise identical."""
+    rows x all V columns within 1e-5 * S; run twice, bitwise identical; the
+    BF16 output is the nearest-even rounding of the FP32 one everywhere."""
     inp = workloads.lmhead_1024()
     _say("lmhead_1024 random logits")
     x, W = dev_bf16(inp.x), dev_bf16(inp.W)
     out = lmh.lmhead_logits(x, W, out_dtype="fp32")
     out2 = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    outb = lmh.lmhead_logits(x, W, out_dtype="bf16")
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(outb.cpu().view(torch.int16), out.cpu().to(torch.bfloat16).view(torch.int16))
     rows = np.concatenate([np.arange(0, 1024, 64), [1, 255, 256, 511, 512, 767, 1022, 1023]])
     L, S = oracle.logits(inp.x, inp.W, rows=rows)
     assert_gemm_close(host_f32(out)[rows], L, S, 1e-5, "fp32 logits 1024")
