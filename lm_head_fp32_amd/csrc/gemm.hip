@@ -552,69 +552,77 @@ struct TrOperand {
     }
 };
 
-// FP32 epilogue through LDS: the tile is written out 32 columns (output rows
-// c) at a time.  The waves owning those columns put their accumulators into a
-// [32][BR] FP32 staging area (the first LDS stage buffer, free once the main
-// loop is done), 16-byte chunk k of row c stored at chunk k ^ (c % 16) so that
-// both the fragment writes and the row reads below hit distinct banks; then
-// every wave reads whole rows and stores them with one 16-byte access per
-// lane, BR * 4 contiguous bytes per row (the register layout of the MFMA
-// result would store 32 bytes into each of 32 rows per instruction).
-// EPI: plain FP32 store, FP32 accumulate (D += tile) or BF16 store (each
-// value rounded to nearest-even in registers, a [32][BR] BF16 staging area,
-// 16 bytes per lane).  Every thread of the workgroup must call this.
+// Epilogue through LDS: the tile is written out in rounds.  In round t every
+// wave puts fragment column t of its accumulators (32 output rows c) into the
+// staging buffer of its wave column (stage, and stage2 when WC == 2: the first
+// LDS stage buffers, free once the main loop is done), a [32][BR] array with
+// 16-byte chunk k of row c stored at chunk k ^ (c % 16) so that both the
+// fragment writes and the row reads below hit distinct banks.  Then every wave
+// reads whole rows and stores them with one 16-byte access per lane (the MFMA
+// result's register layout would store 32 bytes into each of 32 rows per
+// instruction).  EPI: FP32 store, FP32 accumulate (D += tile), or BF16 store
+// (rounded to nearest-even in registers by v_cvt_pk_bf16_f32 and staged as
+// BF16, 8 values per lane and store).  Every thread of the workgroup must call
+// this.
 template <int FR, int FC, int WR, int WC, int BR, int BC, int EPI>
 __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&acc)[FR][FC],
                                                int64_t r0, int64_t c0, int wr, int wc, int lane,
-                                               int wave, void *stage)
+                                               int wave, void *stage, void *stage2)
 {
     constexpr int TR = FR * 32, TC = FC * 32, NW = WR * WC;
-    constexpr int CH = 32;               // tile columns per chunk
-    constexpr int ROWB = BR * 4;         // bytes per staged row
-    constexpr int LPR = BR / 4;          // lanes per row (4 floats each)
-    constexpr int RPI = 64 / LPR;        // rows per wave instruction
+    constexpr bool BF = EPI == static_cast<int>(Epi::kStoreBF16);
+    constexpr int ESZ = BF ? 2 : 4;        // bytes per staged element
+    constexpr int ROWB = BR * ESZ;         // bytes per staged row
+    constexpr int EPC = 16 / ESZ;          // elements per 16-byte chunk
+    constexpr int LPR = BR / EPC;          // lanes per row
+    constexpr int RPI = 64 / LPR;          // rows per wave instruction
+    constexpr int ROWS = 32 * WC;          // rows staged per round
     static_assert(BR == 128 || BR == 256, "staging written for 128- or 256-row tiles");
-    static_assert(TR * WR == BR && TC * WC == BC && BC % CH == 0, "tile shape");
-    char *sb = static_cast<char *>(stage);
+    static_assert(WC == 1 || WC == 2, "one staging buffer per wave column");
+    static_assert(TR * WR == BR && TC * WC == BC, "tile shape");
+    static_assert(ROWS % (NW * RPI) == 0, "whole passes");
+    char *const sb0 = static_cast<char *>(stage);
+    char *const sb1 = static_cast<char *>(WC == 2 ? stage2 : stage);
+    char *const own = wc ? sb1 : sb0;
+    const int cl = lane & 31;
     __syncthreads();  // every wave is done reading the main loop's stages
-    if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
-        // BF16: round in registers (v_cvt_pk_bf16_f32, nearest-even), stage
-        // BR * 2 bytes per row, the 8-byte half h of 16-byte chunk k of row c
-        // at chunk k ^ (c % 16); then 16 bytes (8 values) per lane per store.
-        constexpr int ROWB16 = BR * 2;
-        constexpr int LPR16 = BR / 8;      // lanes per row
-        constexpr int RPI16 = 64 / LPR16;  // rows per wave instruction
 #pragma unroll
-        for (int ch = 0; ch < BC / CH; ++ch) {
-            const int cw = (ch * CH) / TC;
-            const int j = ((ch * CH) % TC) / 32;
-            if (wc == cw) {
-                const int cl = lane & 31;
+    for (int t = 0; t < FC; ++t) {
 #pragma unroll
-                for (int i = 0; i < FR; ++i)
+        for (int i = 0; i < FR; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int rl = wr * TR + i * 32 + q * 8 + (lane >> 5) * 4;
-                        const f32x2 lo = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]};
-                        const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        uint2 w;
-                        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-                        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
-                        *reinterpret_cast<uint2 *>(sb + cl * ROWB16 +
-                                                   (((rl >> 3) ^ (cl & 15)) << 4) +
-                                                   ((rl >> 2) & 1) * 8) = w;
-                    }
+            for (int q = 0; q < 4; ++q) {
+                const int rl = wr * TR + i * 32 + q * 8 + (lane >> 5) * 4;  // 4 rows from rl
+                if constexpr (BF) {
+                    const f32x2 lo = {acc[i][t][4 * q + 0], acc[i][t][4 * q + 1]};
+                    const f32x2 hi = {acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
+                    uint2 w;
+                    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+                    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+                    *reinterpret_cast<uint2 *>(own + cl * ROWB + (((rl >> 3) ^ (cl & 15)) << 4) +
+                                               ((rl >> 2) & 1) * 8) = w;
+                } else {
+                    float4 v;
+                    v.x = acc[i][t][4 * q + 0];
+                    v.y = acc[i][t][4 * q + 1];
+                    v.z = acc[i][t][4 * q + 2];
+                    v.w = acc[i][t][4 * q + 3];
+                    *reinterpret_cast<float4 *>(own + cl * ROWB + (((rl >> 2) ^ (cl & 15)) << 4)) =
+                        v;
+                }
             }
-            __syncthreads();
+        __syncthreads();
 #pragma unroll
-            for (int rr0 = 0; rr0 < CH; rr0 += NW * RPI16) {
-                const int rr = rr0 + wave * RPI16 + lane / LPR16;
-                const int k = lane % LPR16;
-                const int64_t c = c0 + ch * CH + rr;
-                const int64_t r = r0 + 8 * k;
-                if (rr < CH && c < g.C && r < g.R) {
-                    const uint4 v =
-                        *reinterpret_cast<const uint4 *>(sb + rr * ROWB16 + ((k ^ (rr & 15)) << 4));
+        for (int rr0 = 0; rr0 < ROWS; rr0 += NW * RPI) {
+            const int rr = rr0 + wave * RPI + lane / LPR;
+            const int b = rr >> 5, cs = rr & 31;
+            const int k = lane % LPR;
+            const int64_t c = c0 + b * TC + t * 32 + cs;
+            const int64_t r = r0 + EPC * k;
+            const char *src = (b ? sb1 : sb0) + cs * ROWB + ((k ^ (cs & 15)) << 4);
+            if (c < g.C && r < g.R) {
+                if constexpr (BF) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(src);
                     uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
                     if (r + 8 <= g.R) {
                         *reinterpret_cast<uint4 *>(out) = v;
@@ -623,56 +631,24 @@ __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&ac
                         for (int e = 0; e < 8 && r + e < g.R; ++e)
                             out[e] = static_cast<uint16_t>(vv[e >> 1] >> (16 * (e & 1)));
                     }
-                }
-            }
-            __syncthreads();
-        }
-        return;
-    }
-#pragma unroll
-    for (int ch = 0; ch < BC / CH; ++ch) {
-        const int cw = (ch * CH) / TC;        // the wave column that owns the chunk
-        const int j = ((ch * CH) % TC) / 32;  // its fragment column block
-        if (wc == cw) {
-            const int cl = lane & 31;
-#pragma unroll
-            for (int i = 0; i < FR; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int k16 = (wr * TR + i * 32 + q * 8 + (lane >> 5) * 4) >> 2;
-                    float4 v;
-                    v.x = acc[i][j][4 * q + 0];
-                    v.y = acc[i][j][4 * q + 1];
-                    v.z = acc[i][j][4 * q + 2];
-                    v.w = acc[i][j][4 * q + 3];
-                    *reinterpret_cast<float4 *>(sb + cl * ROWB + ((k16 ^ (cl & 15)) << 4)) = v;
-                }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int rr0 = 0; rr0 < CH; rr0 += NW * RPI) {
-            const int rr = rr0 + wave * RPI + lane / LPR;
-            const int k16 = lane % LPR;
-            const int64_t c = c0 + ch * CH + rr;
-            const int64_t r = r0 + 4 * k16;
-            if (rr < CH && c < g.C && r < g.R) {
-                const float4 v = *reinterpret_cast<const float4 *>(sb + rr * ROWB +
-                                                                   ((k16 ^ (rr & 15)) << 4));
-                float *out = static_cast<float *>(g.D) + c * g.ldd + r;
-                if (r + 4 <= g.R) {
-                    float4 w = v;
-                    if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
-                        const float4 o = *reinterpret_cast<const float4 *>(out);
-                        w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
-                    }
-                    *reinterpret_cast<float4 *>(out) = w;
                 } else {
-                    const float vv[4] = {v.x, v.y, v.z, v.w};
-                    for (int e = 0; e < 4 && r + e < g.R; ++e) {
-                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
-                            out[e] = out[e] + vv[e];
-                        else
-                            out[e] = vv[e];
+                    const float4 v = *reinterpret_cast<const float4 *>(src);
+                    float *out = static_cast<float *>(g.D) + c * g.ldd + r;
+                    if (r + 4 <= g.R) {
+                        float4 w = v;
+                        if constexpr (EPI == static_cast<int>(Epi::kAccumF32)) {
+                            const float4 o = *reinterpret_cast<const float4 *>(out);
+                            w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
+                        }
+                        *reinterpret_cast<float4 *>(out) = w;
+                    } else {
+                        const float vv[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e) {
+                            if constexpr (EPI == static_cast<int>(Epi::kAccumF32))
+                                out[e] = out[e] + vv[e];
+                            else
+                                out[e] = vv[e];
+                        }
                     }
                 }
             }
@@ -810,7 +786,7 @@ gemm_big(GemmProblem g, TileMap tm)
     constexpr int FR = TR / 32, FC = TC / 32;
     constexpr int NKK = BK / 16;
     static_assert(BK == 64 && NKK == 4 && FR % 2 == 0, "schedule written for BK = 64");
-    static_assert(32 * BR * 4 <= BR * BK * 2, "the FP32 epilogue stages 32 rows in sA0");
+    static_assert(32 * BR * 4 <= BR * BK * 2, "the FP32 epilogue stages 32 rows in sA0, sA1");
     // p-major operands (AT / BT) are read through transposing LDS loads.
     using OpA = std::conditional_t<AT, TrOperand<BR, BK, NW>, DmaOperand<BR, BK, NW>>;
     using OpB = std::conditional_t<BT, TrOperand<BC, BK, NW>, DmaOperand<BC, BK, NW>>;
@@ -987,10 +963,11 @@ gemm_big(GemmProblem g, TileMap tm)
     if constexpr (EPI == static_cast<int>(Epi::kStoreF32Stats) && !AT && !BT) {
         int32_t yt[FC];
         tile_targets<FR, FC>(g, c0, wc, lane, yt);  // in flight during the stores
-        store_tile_lds<FR, FC, WR, WC, BR, BC, 0>(g, acc, r0, c0, wr, wc, lane, wave, sA0);
+        store_tile_lds<FR, FC, WR, WC, BR, BC, 0>(g, acc, r0, c0, wr, wc, lane, wave, sA0, sA1);
         stats_tile<FR, FC, WR, BC>(g, acc, yt, r0, c0, tr, wr, wc, lane, tid);
     } else {
-        store_tile_lds<FR, FC, WR, WC, BR, BC, EPI>(g, acc, r0, c0, wr, wc, lane, wave, sA0);
+        store_tile_lds<FR, FC, WR, WC, BR, BC, EPI>(g, acc, r0, c0, wr, wc, lane, wave, sA0,
+                                                     sA1);
     }
 }
 
@@ -1137,7 +1114,7 @@ gemm_small(GemmProblem g, TileMap tm)
         compute(sA[b], sB[b]);
     }
     store_tile_lds<FR, FC, NW, 1, BR, BC, EPI>(g, acc, r0, c0, wave, 0, lane, wave,
-                                               sA_c(std::integral_constant<int, 0>{}));
+                                               sA_c(std::integral_constant<int, 0>{}), nullptr);
 }
 
 template <int BC, int S>
@@ -1365,11 +1342,13 @@ gemm_pp(GemmProblem g, TileMap tm)
         int32_t yt[FC];
         tile_targets<FR, FC>(g, c0, grp, lane, yt);  // in flight during the stores
         store_tile_lds<FR, FC, WR, 2, BR, BC, 0>(g, acc, r0, c0, wr, grp, lane, wave,
-                                                 sA(std::integral_constant<int, 0>{}));
+                                                 sA(std::integral_constant<int, 0>{}),
+                                                 sA(std::integral_constant<int, 1>{}));
         stats_tile<FR, FC, WR, BC>(g, acc, yt, r0, c0, tr, wr, grp, lane, tid);
     } else {
         store_tile_lds<FR, FC, WR, 2, BR, BC, EPI>(g, acc, r0, c0, wr, grp, lane, wave,
-                                                   sA(std::integral_constant<int, 0>{}));
+                                                   sA(std::integral_constant<int, 0>{}),
+                                                   sA(std::integral_constant<int, 1>{}));
     }
 }
 
