@@ -54,7 +54,7 @@ PEAK_HBM_GBS = 8000.0
 # counters on this GPU), valid only for the kernel sources they were taken on
 # (code hash of the .hip file, see source_code_hash).  Changed code reports null.
 MEASURED_TRAFFIC = {
-    "logits_fp32": {"src": "gemm.hip", "sha": "13f875068e57d469", "bytes": (2 * 396342 + 131072) * 1024},
+    "logits_fp32": {"src": "gemm.hip", "sha": "98183de989f7a887", "bytes": (2 * 396285 + 131072) * 1024},
     "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "90e3a3bef99ccf2c",
                           "bytes": (2 * 2097954 + 514 + 2 * 2056476 + 4195628) * 1024},
 }
@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the side measurements")
     ap.add_argument("--no-grid", action="store_true",
-                    help="skip the GEMM grid, cold/warm, sustained-peak and vendor measurements")
+                    help="skip the GEMM grid and the cold/warm measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -198,8 +198,11 @@ def gemm_grid(torch, lmh, samples, seed):
 
 def cold_vs_warm(torch, lmh, samples, seed):
     """FP32-out logits GEMM at M=128 K=4096 and M=1024 K=8192 (V=32768), warm
-    (back to back) and cold (a 512 MiB device write between samples, outside
-    the timed events, evicts the operands from L2 and the 256 MB MALL)."""
+    (back to back) and cold: between samples, outside the timed events, a
+    512 MiB device write ("cold_write": the evicted operands are replaced by
+    dirty lines that the GEMM's traffic then writes back) or a 512 MiB read
+    ("cold_read": clean lines) evicts the operands from L2 and the 256 MB
+    MALL."""
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed + 1)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -217,17 +220,22 @@ def cold_vs_warm(torch, lmh, samples, seed):
             tm("warm", f)
         for i in range(samples):
             flush.fill_(i & 0xFF)
-            tm("cold", f)
+            tm("cold_write", f)
+        flush.fill_(1)
+        for i in range(samples):
+            sink = flush.view(torch.int64).sum()
+            tm("cold_read", f)
         torch.cuda.synchronize()
-        w, wp10, wp90 = quantiles(tm.ms("warm"))
-        c, cp10, cp90 = quantiles(tm.ms("cold"))
         flop = 2.0 * M * K * V
-        res[f"{M}x{K}x{V}"] = {"warm_ms": w, "warm_p10_ms": wp10, "warm_p90_ms": wp90,
-                               "cold_ms": c, "cold_p10_ms": cp10, "cold_p90_ms": cp90,
-                               "warm_tflops": flop / (w * 1e-3) / 1e12,
-                               "cold_tflops": flop / (c * 1e-3) / 1e12}
-        log(f"[bench]   {M}x{K}x{V}: warm {w * 1e3:.1f} us, cold {c * 1e3:.1f} us")
-        del W, x, o
+        r = {}
+        for name in ("warm", "cold_write", "cold_read"):
+            med, p10, p90 = quantiles(tm.ms(name))
+            r.update({f"{name}_ms": med, f"{name}_p10_ms": p10, f"{name}_p90_ms": p90,
+                      f"{name}_tflops": flop / (med * 1e-3) / 1e12})
+        res[f"{M}x{K}x{V}"] = r
+        log(f"[bench]   {M}x{K}x{V}: warm {r['warm_ms'] * 1e3:.1f} us, cold (write flush) "
+            f"{r['cold_write_ms'] * 1e3:.1f} us, cold (read flush) {r['cold_read_ms'] * 1e3:.1f} us")
+        del W, x, o, sink
     del flush
     return res
 
@@ -612,6 +620,7 @@ def main():
             f"(K >= 8192: {g['median_fp32_overhead_pct_k_ge_8192']:+.2f} %)")
         log("[bench] logits GEMM cold vs warm")
         out["logits_cold_vs_warm"] = cold_vs_warm(torch, lmh, args.samples, workloads.SEED)
+    if not args.no_side:
         log("[bench] sustained peaks: MFMA loop, device copy")
         out["sustained_peaks"] = sustained_peaks(torch, lmh)
         sp = out["sustained_peaks"]
@@ -638,14 +647,14 @@ def main():
         thr = oracle.default_threads()
         # Bounded samples of the same work (a few seconds each): logits rows
         # of the step workload, and rows of the 8192 x 131072 CE workload.
-        n_rows = min(M, 32 * thr)
+        n_rows = min(M, 64 * thr)
         rows = np.linspace(0, M - 1, n_rows).astype(np.int64)
         log(f"[bench] cpu baseline: oracle logits on {rows.size} of {M} rows, {thr} threads")
         t0 = time.perf_counter()
         oracle.logits(inp.x, inp.W, rows=rows, with_abs=False, nthreads=thr)
         dt = time.perf_counter() - t0
         cpu_tflops = 2.0 * rows.size * K * V / dt / 1e12
-        n_cpu = min(8192, 64 * thr)
+        n_cpu = min(8192, 256 * thr)
         ce = workloads.xent_logits(n_cpu, 131072, sigma=3.0, spike_frac=0.01, spike=30.0,
                                    ignore_frac=0.02, seed=workloads.SEED)
         log(f"[bench] cpu baseline: oracle CE fwd+bwd on {n_cpu} rows x 131072")
