@@ -275,6 +275,40 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
                      int64_t M, int64_t K, int64_t V, void *stream);
 
 /*
+ * lmhead_dgrad_workspace_bytes / lmhead_dgrad_ws -- lmhead_dgrad with the sum
+ * over V split in parts ([MIXED] "What does this PR do?", the GEMMs after the
+ * BF16 cast: the same product dX = dlogits . W).
+ *
+ *  When M x K has too few 256 x 256 output tiles to fill the chip (fewer than
+ *  256, e.g. M = 1024, K = 8192), the V sum is split `splits` ways; every
+ *  split writes an FP32 partial dX into `workspace`, and a second kernel adds
+ *  the partials in split order and stores dX (FP32, or BF16 rounded to
+ *  nearest-even once, from the FP32 sum).  splits == 0 picks the shape's
+ *  default (1, 2 or 4); 1 <= splits <= 16 asks for that many parts of whole
+ *  64-deep stages (fewer when V is small).  The result is deterministic run to
+ *  run; its summation order differs from lmhead_dgrad's, so the two agree
+ *  within the FP32 tolerance, and bitwise on integer inputs.
+ *
+ *  lmhead_dgrad_workspace_bytes returns the workspace bytes that
+ *  lmhead_dgrad_ws needs for (M, K, V, splits): parts x M x K4 x 4 with K4 =
+ *  K rounded up to a multiple of 4, or 0 when the shape runs unsplit; a
+ *  negative LMH_ERR_SHAPE for negative sizes or splits outside [0, 16].
+ *
+ *  lmhead_dgrad_ws takes lmhead_dgrad's arguments plus splits and the
+ *  caller's device workspace (16-byte aligned, workspace_bytes >= the size
+ *  above, else LMH_ERR_ALIGN / LMH_ERR_SHAPE; NULL -> LMH_ERR_NULL).  The
+ *  workspace must not overlap dlogits, W or dX (LMH_ERR_ALIAS); its contents
+ *  on entry do not matter and are garbage afterwards.  When the size above is
+ *  0 the call is lmhead_dgrad and the workspace is not touched.  Two calls that
+ *  share a workspace must be ordered on one stream.
+ */
+int64_t lmhead_dgrad_workspace_bytes(int64_t M, int64_t K, int64_t V, int32_t splits);
+int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t ldw,
+                        void *dX, int64_t ldx, int32_t dx_dtype,
+                        int64_t M, int64_t K, int64_t V, int32_t splits,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * lmhead_wgrad -- weight gradient dW[V x K] (+)= dlogits[M x V]^T . x[M x K]
  *
  *  dlogits BF16 [M x V], ldd >= V;  x BF16 [M x K], ldx >= K;

@@ -24,7 +24,7 @@ __all__ = [
     "LMH_BF16", "LMH_FP32", "LMH_FP16", "STATS_COLS", "LmheadError", "lib", "library_path",
     "lmhead_logits", "lmhead_xent_fwd", "lmhead_xent_mean", "lmhead_xent_bwd",
     "lmhead_dgrad", "lmhead_wgrad", "lmhead_status_str", "lmhead_version",
-    "lmhead_diag_mfma_loop",
+    "lmhead_diag_mfma_loop", "lmhead_dgrad_workspace_bytes",
 ]
 
 LMH_BF16, LMH_FP32, LMH_FP16 = 0, 1, 2
@@ -54,6 +54,9 @@ _SIGNATURES = {
     "lmhead_dgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
     "lmhead_wgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
     "lmhead_diag_mfma_loop": ([_i64, _i64, _vp, _vp], _i32),
+    "lmhead_dgrad_workspace_bytes": ([_i64, _i64, _i64, _i32], _i64),
+    "lmhead_dgrad_ws": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
+                         _vp], _i32),
 }
 
 
@@ -372,8 +375,23 @@ def lmhead_xent_fused(logits, target, dloss, ignore_index=-100, dlogits=None, gr
     return (loss if loss is not False else None), stats, dlogits
 
 
-def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", stream=None):
-    """dX[M, K] = dlogits[M, V] . W[V, K] (bf16 operands, fp32 accumulation)."""
+def lmhead_dgrad_workspace_bytes(M, K, V, splits=0):
+    """Workspace bytes lmhead_dgrad_ws needs for (M, K, V, splits); 0 = unsplit."""
+    n = int(lib().lmhead_dgrad_workspace_bytes(int(M), int(K), int(V), int(splits)))
+    if n < 0:
+        _check("lmhead_dgrad_workspace_bytes", -n)
+    return n
+
+
+def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", splits=0, workspace=None, stream=None):
+    """dX[M, K] = dlogits[M, V] . W[V, K] (bf16 operands, fp32 accumulation).
+
+    splits: 0 = the shape's default split of the V sum (lmhead_dgrad_ws; the
+    FP32 partials go to `workspace`, a CUDA tensor of at least
+    lmhead_dgrad_workspace_bytes(M, K, V, splits) bytes, allocated here from
+    torch's caching allocator on the current stream when not given -- pass one
+    when launching on another stream), 1 = the unsplit kernel (lmhead_dgrad),
+    n = n parts."""
     code = _dtype_code(dx_dtype)
     pd, ldd = _mat(dlogits, "dlogits", torch.bfloat16)
     pw, ldw = _mat(W, "W", torch.bfloat16)
@@ -388,8 +406,20 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", stream=None):
     px, ldx = _mat(dX, "dX", dX.dtype)
     if dX.shape != (M, K):
         raise ValueError("dX must be [M, K]")
-    _check("lmhead_dgrad", lib().lmhead_dgrad(pd, ldd, pw, ldw, px, ldx, code, M, K, V,
-                                              _stream(stream)))
+    splits = int(splits)
+    need = 0 if splits == 1 else lmhead_dgrad_workspace_bytes(M, K, V, splits)
+    if need == 0:
+        _check("lmhead_dgrad", lib().lmhead_dgrad(pd, ldd, pw, ldw, px, ldx, code, M, K, V,
+                                                  _stream(stream)))
+        return dX
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dlogits.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("lmhead_dgrad_ws", lib().lmhead_dgrad_ws(pd, ldd, pw, ldw, px, ldx, code, M, K, V, splits,
+                                                    workspace.data_ptr(), nbytes,
+                                                    _stream(stream)))
     return dX
 
 

@@ -14,6 +14,7 @@ namespace {
 
 constexpr int64_t kMaxDim = static_cast<int64_t>(INT_MAX);
 constexpr int64_t kMaxDiagWorkgroups = 65536;
+constexpr int32_t kMaxSplits = 16;
 
 // Vocabulary columns per cross-entropy record of lmhead_logits_xent (the
 // logits GEMM's tile height).
@@ -102,7 +103,7 @@ const char *lmhead_status_str(int32_t status)
 
 int32_t lmhead_version(void)
 {
-    return 102;
+    return 103;
 }
 
 int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, void *out,
@@ -409,6 +410,58 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
     return launch_status(lmh::launch_gemm_dgrad(
         p, dx_dtype == LMH_FP32 ? lmh::Epi::kStoreF32 : lmh::Epi::kStoreBF16,
         static_cast<hipStream_t>(stream)));
+}
+
+int64_t lmhead_dgrad_workspace_bytes(int64_t M, int64_t K, int64_t V, int32_t splits)
+{
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim || splits < 0 ||
+        splits > kMaxSplits)
+        return -static_cast<int64_t>(LMH_ERR_SHAPE);
+    return 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
+}
+
+int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t ldw, void *dX,
+                        int64_t ldx, int32_t dx_dtype, int64_t M, int64_t K, int64_t V,
+                        int32_t splits, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    LMH_TRY(check_dtype_out(dx_dtype));
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim || splits < 0 ||
+        splits > kMaxSplits || workspace_bytes < 0)
+        return LMH_ERR_SHAPE;
+    const int64_t need = 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
+    if (need == 0)
+        return lmhead_dgrad(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V, stream);
+    const int64_t osz = dx_dtype == LMH_FP32 ? 4 : 2;
+    LMH_TRY(check_matrix(dX, M, K, ldx, dx_dtype == LMH_FP32 ? 4 : 8));
+    LMH_TRY(check_matrix(dlogits, M, V, ldd, 8));
+    LMH_TRY(check_matrix(W, V, K, ldw, 8));
+    if (!workspace)
+        return LMH_ERR_NULL;
+    if (!aligned16(workspace))
+        return LMH_ERR_ALIGN;
+    if (workspace_bytes < need)
+        return LMH_ERR_SHAPE;
+    const Span so = span_of(dX, M, K, ldx, osz);
+    const Span sd = span_of(dlogits, M, V, ldd, 2), sw = span_of(W, V, K, ldw, 2);
+    Span ws;
+    ws.lo = reinterpret_cast<uintptr_t>(workspace);
+    ws.hi = ws.lo + static_cast<uintptr_t>(need);
+    if (overlaps(so, sd) || overlaps(so, sw) || overlaps(ws, so) || overlaps(ws, sd) ||
+        overlaps(ws, sw))
+        return LMH_ERR_ALIAS;
+    lmh::GemmProblem p;
+    p.A = static_cast<const uint16_t *>(W);
+    p.lda = ldw;
+    p.B = static_cast<const uint16_t *>(dlogits);
+    p.ldb = ldd;
+    p.D = dX;
+    p.ldd = ldx;
+    p.R = K;
+    p.C = M;
+    p.P = V;
+    return launch_status(lmh::launch_gemm_dgrad_split(p, dx_dtype != LMH_FP32, splits,
+                                                      static_cast<float *>(workspace),
+                                                      static_cast<hipStream_t>(stream)));
 }
 
 int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ldx, float *dW,

@@ -28,6 +28,11 @@ struct GemmProblem {
     int32_t ignore_index = 0;
     void *part4 = nullptr;
     int64_t part_stride4 = 0;
+    // Split of the sum over p (gemm_big only): workgroup row blockIdx.y sums
+    // p in [y * psplit, min(P, (y + 1) * psplit)) and stores its FP32 partial
+    // tile at D + y * split_stride.  psplit == 0: no split.
+    int64_t psplit = 0;
+    int64_t split_stride = 0;
 };
 
 enum class Epi : int { kStoreF32 = 0, kStoreBF16 = 1, kAccumF32 = 2, kStoreF32Stats = 3 };
@@ -39,6 +44,12 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s);
 // records from the stored logits.
 bool gemm_logits_stats_in_epilogue(const GemmProblem &p);
 hipError_t launch_gemm_dgrad(const GemmProblem &p, Epi epi, hipStream_t s);
+// dgrad with the sum over V split `splits` ways (0 = the shape's default):
+// FP32 partials in `ws`, then a reduction in split order into p.D.
+int dgrad_default_splits(int64_t M, int64_t K, int64_t V);
+int64_t dgrad_workspace_elems(int64_t M, int64_t K, int64_t V, int splits);
+hipError_t launch_gemm_dgrad_split(const GemmProblem &p, bool bf16_out, int splits, float *ws,
+                                   hipStream_t s);
 hipError_t launch_gemm_wgrad(const GemmProblem &p, Epi epi, hipStream_t s);
 
 hipError_t launch_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,

@@ -778,8 +778,18 @@ __device__ __forceinline__ void stats_tile(const GemmProblem &g, f32x16 (&acc)[F
 template <int BR, int BC, int BK, int WR, int WC, bool AT, bool BT, int EPI>
 __global__ void __launch_bounds__(WR * WC * 64)
     __attribute__((amdgpu_waves_per_eu(WR * WC / 4, WR * WC / 4)))
-gemm_big(GemmProblem g, TileMap tm)
+gemm_big(GemmProblem gp, TileMap tm)
 {
+    // Split of the sum over p (blockIdx.y): this workgroup's p range and its
+    // FP32 partial tile (see GemmProblem::psplit).
+    GemmProblem g = gp;
+    if (gp.psplit > 0) {
+        const int64_t p0 = min(static_cast<int64_t>(blockIdx.y) * gp.psplit, gp.P);
+        g.P = min(gp.psplit, gp.P - p0);
+        g.A = gp.A + (AT ? p0 * gp.lda : p0);
+        g.B = gp.B + (BT ? p0 * gp.ldb : p0);
+        g.D = static_cast<float *>(gp.D) + blockIdx.y * gp.split_stride;
+    }
     constexpr int NT = WR * WC * 64;
     constexpr int NW = WR * WC;
     constexpr int TR = BR / WR, TC = BC / WC;
@@ -1382,7 +1392,9 @@ hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
     if (nwg == 0)
         return hipSuccess;
-    dim3 grid(static_cast<unsigned>(nwg)), block(WR * WC * 64);
+    const unsigned nsplit =
+        p.psplit > 0 ? static_cast<unsigned>((p.P + p.psplit - 1) / p.psplit) : 1u;
+    dim3 grid(static_cast<unsigned>(nwg), nsplit), block(WR * WC * 64);
     switch (epi) {
     case Epi::kStoreF32:
         hipLaunchKernelGGL((gemm_big<BR, BC, BK, WR, WC, AT, BT, 0>), grid, block, 0, s, p, tm);
@@ -1521,6 +1533,116 @@ hipError_t launch_gemm_dgrad(const GemmProblem &p, Epi epi, hipStream_t s)
 {
     // R = K (hidden), C = M (tokens), A = W stored [V][K] (p-major).
     return launch_bwd<true, false>(p, epi, s);
+}
+
+// dgrad with the sum over V split in `splits` parts: at M = 1024, K = 8192
+// the 256 x 256 tiles number only 128, so the unsplit path uses 256 x 128
+// tiles (one per CU), which run at ~0.65x the 256 x 256 tile's rate; two
+// splits give 256 workgroups of 256 x 256 tiles.  Each split stores an FP32
+// partial dX into the workspace ([split][M][K4], K4 = K rounded up to 4), and
+// splitk_reduce adds them in split order -- deterministic, but a different
+// summation order from the unsplit kernel.
+int dgrad_default_splits(int64_t M, int64_t K, int64_t V)
+{
+    const int64_t tiles256 = ((K + 255) / 256) * ((M + 255) / 256);
+    if (tiles256 < 64 || tiles256 >= 256 || V < 16384)
+        return 1;
+    return tiles256 >= 128 ? 2 : 4;
+}
+
+namespace {
+
+int64_t split_len(int64_t P, int splits)
+{
+    const int64_t per = (P + splits - 1) / splits;
+    return (per + 63) / 64 * 64;  // whole 64-deep stages
+}
+
+// out[c][r] = sum over z = 0 .. S-1 (in order) of ws[z][c][r], r < R, c < C;
+// pitch R4 in ws.  Each thread takes 4 consecutive r of one row.
+template <bool BF16>
+__global__ void __launch_bounds__(256) splitk_reduce(const float *ws, int S, int64_t stride,
+                                                     int64_t R, int64_t R4, int64_t C, void *D,
+                                                     int64_t ldd)
+{
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t per_row = R4 / 4;
+    const int64_t c = q / per_row;
+    const int64_t r = (q - c * per_row) * 4;
+    if (c >= C)
+        return;
+    const float *src = ws + c * R4 + r;
+    float4 a = *reinterpret_cast<const float4 *>(src);
+    for (int z = 1; z < S; ++z) {
+        const float4 b = *reinterpret_cast<const float4 *>(src + z * stride);
+        a.x += b.x, a.y += b.y, a.z += b.z, a.w += b.w;
+    }
+    const float v[4] = {a.x, a.y, a.z, a.w};
+    if constexpr (BF16) {
+        uint16_t *out = static_cast<uint16_t *>(D) + c * ldd + r;
+        const f32x2 lo = {a.x, a.y}, hi = {a.z, a.w};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+        const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+        if (r + 4 <= R) {
+            *reinterpret_cast<uint2 *>(out) = make_uint2(w0, w1);
+        } else {
+            const uint32_t w[2] = {w0, w1};
+            for (int e = 0; e < 4 && r + e < R; ++e)
+                out[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+        }
+    } else {
+        float *out = static_cast<float *>(D) + c * ldd + r;
+        if (r + 4 <= R) {
+            *reinterpret_cast<float4 *>(out) = a;
+        } else {
+            for (int e = 0; e < 4 && r + e < R; ++e)
+                out[e] = v[e];
+        }
+    }
+}
+
+}  // namespace
+
+int64_t dgrad_workspace_elems(int64_t M, int64_t K, int64_t V, int splits)
+{
+    if (splits <= 0)
+        splits = dgrad_default_splits(M, K, V);
+    if (splits <= 1 || M <= 0 || K <= 0 || V <= 0)
+        return 0;
+    const int64_t ps = split_len(V, splits);
+    const int64_t ns = (V + ps - 1) / ps;
+    return ns * M * ((K + 3) / 4 * 4);
+}
+
+hipError_t launch_gemm_dgrad_split(const GemmProblem &p, bool bf16_out, int splits, float *ws,
+                                   hipStream_t s)
+{
+    // p: R = K, C = M, P = V, D = dX (ldd), as for launch_gemm_dgrad.
+    if (splits <= 0)
+        splits = dgrad_default_splits(p.C, p.R, p.P);
+    if (splits <= 1 || p.P <= 0 || p.R <= 0 || p.C <= 0 || !ws)
+        return launch_gemm_dgrad(p, bf16_out ? Epi::kStoreBF16 : Epi::kStoreF32, s);
+    const int64_t R4 = (p.R + 3) / 4 * 4;
+    GemmProblem q = p;
+    q.psplit = split_len(p.P, splits);
+    q.split_stride = p.C * R4;
+    q.D = ws;
+    q.ldd = R4;
+    const int ns = static_cast<int>((p.P + q.psplit - 1) / q.psplit);
+    if (!big_offsets_fit(q))
+        return launch_gemm_dgrad(p, bf16_out ? Epi::kStoreBF16 : Epi::kStoreF32, s);
+    const hipError_t e = launch_big<256, 256, 4, 2, true, false>(q, Epi::kStoreF32, 8, s);
+    if (e != hipSuccess)
+        return e;
+    const int64_t nthr = p.C * (R4 / 4);
+    const unsigned blocks = static_cast<unsigned>((nthr + 255) / 256);
+    if (bf16_out)
+        hipLaunchKernelGGL(splitk_reduce<true>, dim3(blocks), dim3(256), 0, s, ws, ns,
+                           q.split_stride, p.R, R4, p.C, p.D, p.ldd);
+    else
+        hipLaunchKernelGGL(splitk_reduce<false>, dim3(blocks), dim3(256), 0, s, ws, ns,
+                           q.split_stride, p.R, R4, p.C, p.D, p.ldd);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_wgrad(const GemmProblem &p, Epi epi, hipStream_t s)

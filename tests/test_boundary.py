@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert lmh.lmhead_version() == 102
+    assert lmh.lmhead_version() == 103
     assert lmh.lmhead_status_str(0) == "LMH_OK"
     for s in range(1, 7):
         assert lmh.lmhead_status_str(s).startswith("LMH_ERR_")
@@ -243,6 +243,28 @@ def test_dgrad_wgrad_validation(L):
     assert w(A, 128, B, 64, B, 64, 0, 16, 64, 128, None) == ALIAS
     assert w(None, 128, B, 64, C, 64, 0, 16, 64, 128, None) == NULL
     assert w(None, 128, None, 64, C, 64, 1, 0, 64, 128, None) == OK     # M = 0, accumulate
+
+
+def test_dgrad_workspace_and_split_validation(L):
+    wb = L.lmhead_dgrad_workspace_bytes
+    assert wb(1024, 8192, 32768, 0) == 2 * 1024 * 8192 * 4     # default: two parts
+    assert wb(4096, 16384, 131072, 0) == 0                    # enough tiles: unsplit
+    assert wb(16, 64, 128, 0) == 0
+    assert wb(16, 64, 128, 1) == 0
+    assert wb(16, 66, 1000, 3) == 3 * 16 * 68 * 4             # K rounded up to 4
+    assert wb(16, 64, 100, 4) == 2 * 16 * 64 * 4              # 64-deep parts: only two
+    assert wb(-1, 64, 128, 0) == -SHAPE and wb(16, 64, 128, 17) == -SHAPE
+    f = L.lmhead_dgrad_ws
+    need = wb(16, 64, 1000, 2)
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, None, need, None) == NULL
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, D + 4, need, None) == ALIGN
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, D, need - 16, None) == SHAPE
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, C, need, None) == ALIAS   # on dX
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, A + 64, need, None) == ALIAS
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, -1, D, need, None) == SHAPE
+    assert f(A, 1000, B, 64, C, 64, FP16, 16, 64, 1000, 2, D, need, None) == DTYPE
+    # unsplit shape: the call is lmhead_dgrad (its own checks), the workspace unused
+    assert f(A, 120, B, 64, C, 64, BF16, 16, 64, 128, 0, None, 0, None) == SHAPE  # ldd < V
 
 
 def test_diag_mfma_loop_validation(L):

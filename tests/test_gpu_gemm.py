@@ -186,6 +186,54 @@ def test_dgrad_random_sampled():
     assert_gemm_close(host_f32(dx)[rows], ref, S, 1e-5, "dgrad")
 
 
+@pytest.mark.parametrize("M,K,V,splits", [(16, 64, 1000, 2), (33, 72, 1000, 3), (130, 256, 4100, 4),
+                                          (9, 20, 100, 4), (64, 8, 640, 16), (300, 520, 2000, 2)])
+def test_dgrad_split_integer_exact(M, K, V, splits):
+    """The V-split dgrad (FP32 partials in a workspace, then a reduction in
+    split order): bit-exact on integers for FP32 and BF16 dX, ragged M, K, V,
+    padded leading dimensions, a NaN-filled workspace (its contents on entry
+    and its padding columns must not leak into dX)."""
+    dl_bits, W_bits = workloads.integer_operands([(M, V), (V, K)], seed=11 + M + K + V)
+    _say(f"dgrad split={splits} int M={M} K={K} V={V}")
+    dl, W = dev_bf16(dl_bits, _up(V, 8) + 8), dev_bf16(W_bits, _up(K, 8) + 16)
+    need = lmh.lmhead_dgrad_workspace_bytes(M, K, V, splits)
+    assert need > 0
+    ws = torch.full((need // 4 + 64,), float("nan"), device="cuda")
+    dx = padded_out(M, K, _up(K, 4) + 4, torch.float32)
+    lmh.lmhead_dgrad(dl, W, dX=dx, dx_dtype="fp32", splits=splits, workspace=ws)
+    dxb = padded_out(M, K, _up(K, 8) + 8, torch.bfloat16)
+    lmh.lmhead_dgrad(dl, W, dX=dxb, dx_dtype="bf16", splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.dgrad(dl_bits, W_bits)
+    assert np.array_equal(_f32_bits(host_f32(dx)), _f32_bits(ref.astype(np.float32)))
+    assert np.array_equal(host_bits(dxb), oracle.round_bf16(ref))
+    assert padding_untouched(dx) and padding_untouched(dxb)
+
+
+def test_dgrad_split_vs_unsplit_benchmark_shape():
+    """M=1024, K=8192, V=32768 (the step's dgrad): the default path splits V in
+    two; it and the unsplit kernel are both within 1e-5 * S of the FP64 sum on
+    sampled rows, the split path is bitwise repeatable, and its BF16 dX is the
+    nearest-even rounding of its FP32 dX."""
+    rng = np.random.default_rng(workloads.SEED + 5)
+    dl_bits = workloads.normal_bf16(rng, (1024, 32768), 1e-3)
+    W_bits = workloads.normal_bf16(rng, (32768, 8192), 0.02)
+    assert lmh.lmhead_dgrad_workspace_bytes(1024, 8192, 32768) == 2 * 1024 * 8192 * 4
+    dl, W = dev_bf16(dl_bits), dev_bf16(W_bits)
+    _say("dgrad split vs unsplit 1024x8192x32768")
+    d_split = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32")
+    d_split2 = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32")
+    d_one = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32", splits=1)
+    d_bf = lmh.lmhead_dgrad(dl, W)
+    torch.cuda.synchronize()
+    assert torch.equal(d_split.view(torch.int32), d_split2.view(torch.int32))
+    assert torch.equal(d_bf.cpu().view(torch.int16), d_split.cpu().to(torch.bfloat16).view(torch.int16))
+    rows = np.array([0, 1, 255, 256, 700, 1023])
+    ref, S = oracle.dgrad(dl_bits, W_bits, rows=rows)
+    assert_gemm_close(host_f32(d_split)[rows], ref, S, 1e-5, "dgrad split")
+    assert_gemm_close(host_f32(d_one)[rows], ref, S, 1e-5, "dgrad unsplit")
+
+
 # ------------------------------------------------------------------ wgrad
 
 @pytest.mark.parametrize("M,K,V", [(16, 64, 128), (33, 72, 136), (130, 256, 1000), (8, 8, 8),
