@@ -234,6 +234,34 @@ def test_dgrad_split_vs_unsplit_benchmark_shape():
     assert_gemm_close(host_f32(d_one)[rows], ref, S, 1e-5, "dgrad unsplit")
 
 
+# Leading dimension whose byte offsets within a 256-row tile pass the 32-bit
+# range of buffer loads: (256 * ld + 64) * 2 >= 2^31.
+HUGE_LD = (1 << 22) + 8
+
+
+def test_gemm_generic_fallback_huge_leading_dims():
+    """With leading dimensions of 4,194,312 elements, the logits, dgrad (split
+    or not) and wgrad calls run the generic register-staged kernel: bit-exact
+    on integers, against the oracle."""
+    M, K, V = 5, 72, 40
+    x_bits, W_bits, dl_bits = workloads.integer_operands([(M, K), (V, K), (M, V)], seed=99)
+    _say("gemm generic fallback, huge ld")
+    x, W = dev_bf16(x_bits, HUGE_LD), dev_bf16(W_bits, HUGE_LD)  # 42 MB and 336 MB buffers
+    dl = dev_bf16(dl_bits)
+    out = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    dx = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32", splits=1)
+    dx2 = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32", splits=2)
+    dw = lmh.lmhead_wgrad(dl, x)
+    torch.cuda.synchronize()
+    L, _ = oracle.logits(x_bits, W_bits)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(L.astype(np.float32)))
+    ref, _ = oracle.dgrad(dl_bits, W_bits)
+    assert np.array_equal(_f32_bits(host_f32(dx)), _f32_bits(ref.astype(np.float32)))
+    assert np.array_equal(_f32_bits(host_f32(dx2)), _f32_bits(ref.astype(np.float32)))
+    ref, _ = oracle.wgrad(dl_bits, x_bits)
+    assert np.array_equal(_f32_bits(host_f32(dw)), _f32_bits(ref.astype(np.float32)))
+
+
 # ------------------------------------------------------------------ wgrad
 
 @pytest.mark.parametrize("M,K,V", [(16, 64, 128), (33, 72, 136), (130, 256, 1000), (8, 8, 8),
