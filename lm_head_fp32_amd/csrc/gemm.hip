@@ -1362,6 +1362,194 @@ gemm_pp(GemmProblem g, TileMap tm)
     }
 }
 
+// ---------------------------------------------------------------------------
+// gemm_rows: the logits GEMM for at most 16 tokens, bound by streaming W once
+// from HBM.  Reading W as gemm_small does -- every workgroup walking its 128
+// rows together in 128-byte steps, so all V rows are open in DRAM at once --
+// measured ~4.4 TB/s; reading 32 rows at a time, each over the whole of K in
+// 1 KiB steps, ~5.8 TB/s.  So each workgroup (4 waves) takes groups of 32
+// vocabulary rows one after another and streams each group over K in stages
+// of 512: W [32][512] and the tokens' x [16][512] (tokens past M repeat the
+// last one and are never stored) by direct loads into a ring of three stages
+// (48 KiB each; with the partial-sum area, all 160 KiB of LDS).  Wave w multiplies k range [128 w, 128 w + 128)
+// of every stage (8 MFMAs of 32 x 32 x 16), so the four waves hold partial
+// sums of the same 32 x 32 block; after a group's last stage they are added
+// through LDS and stored, while the next group's first stages load.  LDS rows
+// are 1 KiB; 16-byte chunk c of staged row q sits at chunk c ^ (q % 16), so
+// the 16 lanes of a fragment read hit distinct banks.
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_rows(GemmProblem g, int groups_per_wg)
+{
+    constexpr int XR = 16, S = 3;
+    constexpr int RG = 32, BKS = 512;
+    constexpr int SLOT = (RG + XR) * BKS;     // BF16 elements per stage (W rows, then x)
+    constexpr int NDMA = (RG + XR) / 4;       // direct loads (one staged row each) per wave
+    static_assert(S * SLOT * 2 + 4 * 32 * 32 * 4 <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint16_t ring[S * SLOT];
+    __shared__ __attribute__((aligned(16))) float red[4][32][32];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t ngroups = (g.R + RG - 1) / RG;
+    const int64_t gfirst = static_cast<int64_t>(blockIdx.x) * groups_per_wg;
+    const int ng = static_cast<int>(min(static_cast<int64_t>(groups_per_wg), ngroups - gfirst));
+    const int nks = static_cast<int>(g.P / BKS);
+    const int T = ng * nks;
+
+    // Direct loads of this wave: staged rows q = wave * NDMA + i.  W rows
+    // past V and token rows past M repeat the last valid row.
+    const __amdgpu_buffer_rsrc_t rsX = tile_rsrc(g.B);
+    uint32_t offW[NDMA], offX[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int q = wave * NDMA + i;
+        const int sw = q & 15;
+        const uint32_t gc = static_cast<uint32_t>(lane ^ sw);  // global chunk of this lane
+        offW[i] = static_cast<uint32_t>(q < RG ? (q * g.lda + gc * 8) * 2 : 0);
+        const int64_t tok = min(static_cast<int64_t>(q - RG), g.C - 1);
+        offX[i] = static_cast<uint32_t>(q >= RG ? (tok * g.ldb + gc * 8) * 2 : 0);
+    }
+    auto issue = [&](int t) {
+        const int gi = t / nks, ks = t - gi * nks;
+        const int64_t row0 = (gfirst + gi) * RG;
+        const int soff = ks * BKS * 2;
+        uint16_t *st = ring + (t % S) * SLOT;
+        // W rows of this group past V: clamp the group base so that every
+        // row read lies inside W (those rows' results are not stored).
+        const int64_t wbase = min(row0, g.R - RG > 0 ? g.R - RG : 0);
+        const __amdgpu_buffer_rsrc_t rsW = tile_rsrc(g.A + wbase * g.lda);
+        const int rshift = static_cast<int>(row0 - wbase);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int q = wave * NDMA + i;
+            if (q < RG) {
+                const int qr = min(q + rshift, static_cast<int>(min<int64_t>(g.R - wbase, RG)) - 1);
+                const uint32_t off = offW[i] + static_cast<uint32_t>(((qr - q) * g.lda) * 2);
+                dma16_untracked(rsW, lds_addr(st + q * BKS), off, soff);
+            } else {
+                dma16_untracked(rsX, lds_addr(st + q * BKS), offX[i], soff);
+            }
+        }
+    };
+
+    const int lrow = lane & 31, kh = lane >> 5;
+    const int xrow = lrow & 15;  // MFMA token columns 16 .. 31 repeat 0 .. 15 (not stored)
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        acc[e] = 0.0f;
+
+    // Prologue: stages 0 .. S-2 in flight.
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        if (t < T)
+            issue(t);
+    for (int t = 0; t < T; ++t) {
+        // This wave's loads of stage t have landed (stages t+1 .. t+S-2 may
+        // still be in flight), then every wave's; the slot of stage t-1 is
+        // free once every wave is past this barrier.
+        if (t + S - 2 < T)
+            vm_wait<(S - 2) * NDMA>();
+        else
+            vm_wait<0>();
+        pp_barrier();
+        if (t + S - 1 < T)
+            issue(t + S - 1);
+        const uint16_t *st = ring + (t % S) * SLOT;
+        const uint16_t *sW = st + lrow * BKS;
+        const uint16_t *sX = st + (RG + xrow) * BKS;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = 16 * wave + 2 * j + kh;  // chunk of k = 128 wave + 16 j + 8 kh
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sW + ((c ^ (lrow & 15)) * 8));
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(sX + ((c ^ ((RG + xrow) & 15)) * 8));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
+        if ((t + 1) % nks == 0) {
+            // Last stage of group gi: add the four waves' partial sums.
+            // Lane l holds token l % 32 at rows 8 q + 4 (l / 32) + e.
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 v;
+                v.x = acc[4 * q + 0];
+                v.y = acc[4 * q + 1];
+                v.z = acc[4 * q + 2];
+                v.w = acc[4 * q + 3];
+                *reinterpret_cast<float4 *>(&red[wave][lrow][8 * q + 4 * kh]) = v;
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[e] = 0.0f;
+            pp_barrier();
+            const int c = tid >> 3, r4 = (tid & 7) * 4;
+            float4 sum = *reinterpret_cast<const float4 *>(&red[0][c][r4]);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                const float4 v = *reinterpret_cast<const float4 *>(&red[w][c][r4]);
+                sum.x += v.x, sum.y += v.y, sum.z += v.z, sum.w += v.w;
+            }
+            const int64_t r = (gfirst + t / nks) * RG + r4;
+            if (c < g.C && r < g.R) {
+                const float vv[4] = {sum.x, sum.y, sum.z, sum.w};
+                if constexpr (EPI == static_cast<int>(Epi::kStoreBF16)) {
+                    uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
+                    const f32x2 lo = {sum.x, sum.y}, hi = {sum.z, sum.w};
+                    const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+                    const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+                    if (r + 4 <= g.R) {
+                        *reinterpret_cast<uint2 *>(out) = make_uint2(w0, w1);
+                    } else {
+                        const uint32_t ww[2] = {w0, w1};
+                        for (int e = 0; e < 4 && r + e < g.R; ++e)
+                            out[e] = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
+                    }
+                } else {
+                    float *out = static_cast<float *>(g.D) + c * g.ldd + r;
+                    if (r + 4 <= g.R) {
+                        *reinterpret_cast<float4 *>(out) = sum;
+                    } else {
+                        for (int e = 0; e < 4 && r + e < g.R; ++e)
+                            out[e] = vv[e];
+                    }
+                }
+            }
+            // red is rewritten only after the next group's last stage, past
+            // at least one more barrier.
+        }
+    }
+}
+
+// gemm_rows applies: at most 16 tokens, K a multiple of 512, and 32-bit
+// buffer offsets for 32 W rows and 16 x rows plus K.  It is routed where it
+// measured ahead of gemm_small on MI355X (same box, V = 32768): K >= 8192
+// (+9 to +19 %, W larger than the 256 MB MALL).  At K <= 4096 it was 8 - 14 %
+// behind (W stays in the MALL between calls) and, with 32 staged tokens,
+// 3 % behind at M = 32, so gemm_small keeps those shapes.
+bool rows_fits(const GemmProblem &p)
+{
+    return p.C >= 1 && p.C <= 16 && p.P >= 512 && p.P % 512 == 0 && p.R >= 1 &&
+           (32 * std::max(p.lda, p.ldb) + p.P) * 2 < (int64_t(1) << 31);
+}
+
+bool rows_preferred(const GemmProblem &p)
+{
+    return rows_fits(p) && p.P >= 8192;
+}
+
+hipError_t launch_rows(const GemmProblem &p, Epi epi, hipStream_t s)
+{
+    const int64_t ngroups = (p.R + 31) / 32;
+    const int64_t target_wg = 256;
+    const int gpw = static_cast<int>(std::max<int64_t>(1, (ngroups + target_wg - 1) / target_wg));
+    const unsigned nwg = static_cast<unsigned>((ngroups + gpw - 1) / gpw);
+    if (epi == Epi::kStoreBF16)
+        hipLaunchKernelGGL((gemm_rows<1>), dim3(nwg), dim3(256), 0, s, p, gpw);
+    else
+        hipLaunchKernelGGL((gemm_rows<0>), dim3(nwg), dim3(256), 0, s, p, gpw);
+    return hipGetLastError();
+}
+
 hipError_t launch_pp(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
     TileMap tm;
@@ -1485,6 +1673,12 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 #ifndef LMH_SMALL_S128
 #define LMH_SMALL_S128 5
 #endif
+#ifndef LMH_ROWS
+#define LMH_ROWS 1
+#endif
+    if ((LMH_ROWS == 2 ? rows_fits(p) : LMH_ROWS && rows_preferred(p)) &&
+        (epi == Epi::kStoreF32 || epi == Epi::kStoreBF16))
+        return launch_rows(p, epi, s);
     if (p.C <= 32)
         return launch_small<32, LMH_SMALL_S32>(p, epi, 8, s);
     if (p.C <= 64)

@@ -98,6 +98,30 @@ def test_logits_ragged_integer_exact(M, K, V, pad):
     assert padding_untouched(out) and padding_untouched(outb)
 
 
+@pytest.mark.parametrize("M,K,V,pad", [(1, 8192, 1, 0), (5, 8192, 33, 8), (16, 8192, 1000, 16),
+                                       (9, 16384, 4097, 0), (2, 8192, 65, 24),
+                                       (16, 8192, 40000, 8), (3, 8192, 131072, 0)])
+def test_logits_row_group_kernel_integer_exact(M, K, V, pad):
+    """The few-token kernel that streams 32 vocabulary rows at a time (M <= 16,
+    K >= 8192, a multiple of 512): ragged V (a partial last row group, fewer
+    than 32 rows in all), M from 1 to 16, padded leading dimensions, several
+    row groups per workgroup (V = 40000, 131072); bit-exact FP32 and BF16
+    logits on integers (|logit| <= 64 K < 2^24)."""
+    x_bits, W_bits = workloads.integer_operands([(M, K), (V, K)], seed=23 + M + K + V)
+    _say(f"logits rows M={M} K={K} V={V} pad={pad}")
+    x = dev_bf16(x_bits, K + pad)
+    W = dev_bf16(W_bits, K + 2 * pad)
+    out = padded_out(M, V, _up(V, 4) + 4, torch.float32)
+    lmh.lmhead_logits(x, W, out=out, out_dtype="fp32")
+    outb = padded_out(M, V, _up(V, 8) + 8, torch.bfloat16)
+    lmh.lmhead_logits(x, W, out=outb, out_dtype="bf16")
+    torch.cuda.synchronize()
+    L, _ = oracle.logits(x_bits, W_bits)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(L.astype(np.float32)))
+    assert np.array_equal(host_bits(outb), oracle.round_bf16(L))
+    assert padding_untouched(out) and padding_untouched(outb)
+
+
 def test_logits_k_zero_writes_zeros():
     x = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
     W = torch.empty((12, 0), dtype=torch.bfloat16, device="cuda")
