@@ -26,6 +26,7 @@ half of the metric.  Beside the step the same run measures:
   fraction, and the median FP32-output overhead;
 * the logits GEMM cold (L2 and MALL flushed between samples) and warm at
   M=128 K=4096 and M=1024 K=8192;
+* the full step at M=4096 K=16384 V=131072 (per-kernel times);
 * what the chip sustains: a register-only MFMA loop and a 1 GiB copy; and
   the vendor BLAS on the step's GEMM (BF16 out), for context;
 * the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
@@ -290,6 +291,61 @@ def vendor_context(torch, x, W, M, K, V, samples):
     return {"what": "torch.mm (hipBLASLt), BF16 x BF16 -> BF16 out, same x and W as the step",
             "ms_median": med, "p10_ms": p10, "p90_ms": p90,
             "tflops": 2.0 * M * K * V / (med * 1e-3) / 1e12}
+
+
+def step_4096(torch, lmh, steps, seed):
+    """The full step at M=4096 K=16384 V=131072 (x ~ N(0,1), W ~ N(0, 0.01^2)
+    BF16 from torch's device generator, targets uniform, none ignored):
+    FP32 logits -> CE fwd -> mean -> CE bwd (BF16 dlogits) -> dgrad -> wgrad,
+    per-kernel HIP-event times (medians) over `steps` steps after one warmup."""
+    M, K, V = 4096, 16384, 131072
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 5)
+    x = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+    W = (torch.randn(V, K, device="cuda", generator=gen) * 0.01).to(torch.bfloat16)
+    tgt = torch.randint(0, V, (M,), device="cuda", generator=gen, dtype=torch.int32)
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    loss = torch.empty((M,), dtype=torch.float32, device="cuda")
+    stats = torch.empty((M, 4), dtype=torch.float32, device="cuda")
+    mean = torch.empty((1,), dtype=torch.float32, device="cuda")
+    inv = torch.empty((1,), dtype=torch.float32, device="cuda")
+    dlog = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((V, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(lmh.lmhead_dgrad_workspace_bytes(M, K, V), 16), dtype=torch.uint8,
+                     device="cuda")
+
+    def one(tm):
+        tm("logits", lambda: lmh.lmhead_logits(x, W, out=logits, out_dtype="fp32"))
+        tm("xent_fwd", lambda: lmh.lmhead_xent_fwd(logits, tgt, -100, loss=loss, stats=stats))
+        tm("xent_mean", lambda: lmh.lmhead_xent_mean(loss, tgt, -100, mean=mean, inv_nvalid=inv))
+        tm("xent_bwd", lambda: lmh.lmhead_xent_bwd(logits, stats, tgt, inv, -100, dlogits=dlog,
+                                                   grad_dtype="bf16"))
+        tm("dgrad", lambda: lmh.lmhead_dgrad(dlog, W, dX=dX, dx_dtype="bf16", workspace=ws))
+        tm("wgrad", lambda: lmh.lmhead_wgrad(dlog, x, dW=dW))
+
+    one(KernelTimer(torch))
+    torch.cuda.synchronize()
+    tm = KernelTimer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one(tm)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    flop = 2.0 * M * K * V
+    res = {"workload": "M=4096 K=16384 V=131072 full step", "ms_per_step": 1e3 * wall,
+           "gemm_tflops_per_step": 3 * flop / wall / 1e12}
+    for name in ("logits", "xent_fwd", "xent_mean", "xent_bwd", "dgrad", "wgrad"):
+        med = statistics.median(tm.ms(name))
+        res[f"{name}_ms"] = med
+        if name in ("logits", "dgrad", "wgrad"):
+            res[f"{name}_tflops"] = flop / (med * 1e-3) / 1e12
+    n = M * V
+    res["ce_fwd_bwd_gbps"] = (4.0 * n + 24 * M + 4.0 * n + 2.0 * n + 24 * M) / (
+        (res["xent_fwd_ms"] + res["xent_bwd_ms"]) * 1e-3) / 1e9
+    del x, W, tgt, logits, loss, stats, mean, inv, dlog, dX, dW, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def dev_bf16(torch, np, bits):
@@ -623,6 +679,13 @@ def main():
             f"(K >= 8192: {g['median_fp32_overhead_pct_k_ge_8192']:+.2f} %)")
         log("[bench] logits GEMM cold vs warm")
         out["logits_cold_vs_warm"] = cold_vs_warm(torch, lmh, args.samples, workloads.SEED)
+    if not args.no_side and not args.no_grid:
+        log("[bench] the full step at M=4096 K=16384 V=131072")
+        out["step_4096"] = step_4096(torch, lmh, 3, workloads.SEED)
+        s4 = out["step_4096"]
+        log(f"[bench]   {s4['ms_per_step']:.2f} ms per step; logits {s4['logits_tflops']:.0f}, "
+            f"dgrad {s4['dgrad_tflops']:.0f}, wgrad {s4['wgrad_tflops']:.0f} TFLOPS; CE "
+            f"{s4['ce_fwd_bwd_gbps']:.0f} GB/s")
     if not args.no_side:
         log("[bench] sustained peaks: MFMA loop, device copy")
         out["sustained_peaks"] = sustained_peaks(torch, lmh)
