@@ -21,6 +21,9 @@
 //    by direct buffer loads; the logits GEMM for longer K, and dgrad and wgrad
 //    (p-major operands read through transposing LDS loads).
 //  * gemm_small -- the logits GEMM for few tokens (W streamed once).
+//  * gemm_rows -- the logits GEMM for at most 16 tokens and K >= 8192: W
+//    streamed 32 rows at a time, K split across the waves.
+//  * splitk_reduce -- adds dgrad's FP32 partial sums (V split) in order.
 //  * gemm_kernel -- the generic register-staged form, used only when an
 //    operand's byte offsets exceed the 32-bit range of buffer loads.
 // Workgroup -> tile mapping: the hardware deals consecutive workgroup ids
@@ -1133,7 +1136,7 @@ hipError_t launch_small(const GemmProblem &p, Epi epi, int group_r, hipStream_t 
     TileMap tm;
     tm.tiles_r = static_cast<int>((p.R + 127) / 128);
     tm.tiles_c = static_cast<int>((p.C + BC - 1) / BC);
-    tm.group_r = group_r < 1 ? 1 : group_r;
+    tm.group_r = std::min(std::max(group_r, 1), std::max(tm.tiles_r, 1));
     const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
     if (nwg == 0)
         return hipSuccess;
@@ -1555,7 +1558,7 @@ hipError_t launch_pp(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     TileMap tm;
     tm.tiles_r = static_cast<int>((p.R + 255) / 256);
     tm.tiles_c = static_cast<int>((p.C + 255) / 256);
-    tm.group_r = group_r < 1 ? 1 : group_r;
+    tm.group_r = std::min(std::max(group_r, 1), std::max(tm.tiles_r, 1));
     const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
     if (nwg == 0)
         return hipSuccess;
@@ -1576,7 +1579,7 @@ hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     TileMap tm;
     tm.tiles_r = static_cast<int>((p.R + BR - 1) / BR);
     tm.tiles_c = static_cast<int>((p.C + BC - 1) / BC);
-    tm.group_r = group_r < 1 ? 1 : group_r;
+    tm.group_r = std::min(std::max(group_r, 1), std::max(tm.tiles_r, 1));
     const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
     if (nwg == 0)
         return hipSuccess;
@@ -1610,7 +1613,7 @@ hipError_t launch_cfg(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     TileMap tm;
     tm.tiles_r = static_cast<int>((p.R + BR - 1) / BR);
     tm.tiles_c = static_cast<int>((p.C + BC - 1) / BC);
-    tm.group_r = group_r < 1 ? 1 : group_r;
+    tm.group_r = std::min(std::max(group_r, 1), std::max(tm.tiles_r, 1));
     const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
     if (nwg == 0)
         return hipSuccess;
@@ -1714,10 +1717,13 @@ hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
     case 4: return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
     default: break;
     }
+#ifndef LMH_WGRAD_GROUP
+#define LMH_WGRAD_GROUP 8
+#endif
     const int64_t tiles256 = ((p.R + 255) / 256) * ((p.C + 255) / 256);
     const int64_t tiles256x128 = ((p.R + 255) / 256) * ((p.C + 127) / 128);
     if (tiles256 >= 256)
-        return launch_big<256, 256, 4, 2, AT, BT>(p, epi, 8, s);
+        return launch_big<256, 256, 4, 2, AT, BT>(p, epi, BT ? LMH_WGRAD_GROUP : 8, s);
     if (tiles256x128 >= 192)
         return launch_big<256, 128, 4, 2, AT, BT>(p, epi, 8, s);
     return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
