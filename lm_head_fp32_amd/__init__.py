@@ -389,9 +389,9 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", splits=0, workspace=None,
     splits: 0 = the shape's default split of the V sum (lmhead_dgrad_ws; the
     FP32 partials go to `workspace`, a CUDA tensor of at least
     lmhead_dgrad_workspace_bytes(M, K, V, splits) bytes, allocated here from
-    torch's caching allocator on the current stream when not given -- pass one
-    when launching on another stream), 1 = the unsplit kernel (lmhead_dgrad),
-    n = n parts."""
+    torch's caching allocator when not given and marked as in use on the
+    launch stream; a raw stream handle needs an explicit workspace),
+    1 = the unsplit kernel (lmhead_dgrad), n = n parts."""
     code = _dtype_code(dx_dtype)
     pd, ldd = _mat(dlogits, "dlogits", torch.bfloat16)
     pw, ldw = _mat(W, "W", torch.bfloat16)
@@ -413,7 +413,13 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", splits=0, workspace=None,
                                                   _stream(stream)))
         return dX
     if workspace is None:
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            raise ValueError("lmhead_dgrad on a raw stream handle needs an explicit workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=dlogits.device)
+        if stream is not None:
+            # freed on return: keep the allocator from reusing it before the
+            # kernels on `stream` are done
+            workspace.record_stream(stream)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor")
     nbytes = workspace.numel() * workspace.element_size()

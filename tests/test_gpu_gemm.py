@@ -258,6 +258,26 @@ def test_dgrad_split_vs_unsplit_benchmark_shape():
     assert_gemm_close(host_f32(d_one)[rows], ref, S, 1e-5, "dgrad unsplit")
 
 
+def test_dgrad_split_on_a_side_stream():
+    """The split dgrad launched on another stream with the binding's own
+    workspace (marked in use on that stream) equals the same call on the
+    current stream bitwise; a raw stream handle without a workspace is refused."""
+    M, K, V = 512, 8192, 16384
+    assert lmh.lmhead_dgrad_workspace_bytes(M, K, V) == 4 * M * K * 4  # four parts
+    rng = np.random.default_rng(workloads.SEED + 9)
+    dl = dev_bf16(workloads.normal_bf16(rng, (M, V), 1e-3))
+    W = dev_bf16(workloads.normal_bf16(rng, (V, K), 0.02))
+    ref = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = lmh.lmhead_dgrad(dl, W, dx_dtype="fp32", stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
+    with pytest.raises(ValueError):
+        lmh.lmhead_dgrad(dl, W, dx_dtype="fp32", stream=side.cuda_stream)
+
+
 # Leading dimension whose byte offsets within a 256-row tile pass the 32-bit
 # range of buffer loads: (256 * ld + 64) * 2 >= 2^31.
 HUGE_LD = (1 << 22) + 8
