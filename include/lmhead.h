@@ -280,11 +280,13 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
  * BF16 cast: the same product dX = dlogits . W).
  *
  *  When M x K has too few 256 x 256 output tiles to fill the chip (fewer than
- *  256, e.g. M = 1024, K = 8192), the V sum is split `splits` ways; every
+ *  256, e.g. M = 1024, K = 8192, or few tokens), the V sum is split `splits`
+ *  ways; every
  *  split writes an FP32 partial dX into `workspace`, and a second kernel adds
  *  the partials in split order and stores dX (FP32, or BF16 rounded to
  *  nearest-even once, from the FP32 sum).  splits == 0 picks the shape's
- *  default (1, 2 or 4); 1 <= splits <= 16 asks for that many parts of whole
+ *  default (1 - 16 parts, for ~256 workgroups); 1 <= splits <= 16 asks for
+ *  that many parts of whole
  *  64-deep stages (fewer when V is small).  The result is deterministic run to
  *  run; its summation order differs from lmhead_dgrad's, so the two agree
  *  within the FP32 tolerance, and bitwise on integer inputs.

@@ -1738,16 +1738,29 @@ hipError_t launch_gemm_dgrad(const GemmProblem &p, Epi epi, hipStream_t s)
 // dgrad with the sum over V split in `splits` parts: at M = 1024, K = 8192
 // the 256 x 256 tiles number only 128, so the unsplit path uses 256 x 128
 // tiles (one per CU), which run at ~0.65x the 256 x 256 tile's rate; two
-// splits give 256 workgroups of 256 x 256 tiles.  Each split stores an FP32
+// splits give 256 workgroups of 256 x 256 tiles.  With fewer tokens the
+// unsplit kernel leaves most CUs idle (M = 128, K = 4096: 32 workgroups).  Each split stores an FP32
 // partial dX into the workspace ([split][M][K4], K4 = K rounded up to 4), and
 // splitk_reduce adds them in split order -- deterministic, but a different
 // summation order from the unsplit kernel.
+// Output tiles of the split kernel: 256 x 256, or 256 x 128 for M <= 128.
+int64_t dgrad_split_tiles(int64_t M, int64_t K)
+{
+    return ((K + 255) / 256) * (M <= 128 ? (M + 127) / 128 : (M + 255) / 256);
+}
+
+// Parts: enough for ~256 workgroups (a power of two, at most 16), each at
+// least 2048 deep in V.  Measured on MI355X (same box): M=1024 K=8192 V=32768
+// two parts, 0.61 -> 0.45 ms; M=512 four, 449 -> 266 us; M=256 eight, 447 ->
+// 153 us; M=128 K=4096 sixteen, 370 -> 75 us; M=16 K=4096 sixteen, 306 -> 61
+// us.  256 or more tiles run unsplit.
 int dgrad_default_splits(int64_t M, int64_t K, int64_t V)
 {
-    const int64_t tiles256 = ((K + 255) / 256) * ((M + 255) / 256);
-    if (tiles256 < 64 || tiles256 >= 256 || V < 16384)
-        return 1;
-    return tiles256 >= 128 ? 2 : 4;
+    const int64_t tiles = dgrad_split_tiles(M, K);
+    int s = 1;
+    while (s < 16 && tiles * s * 2 <= 256 && V / (s * 2) >= 2048)
+        s *= 2;
+    return s;
 }
 
 namespace {
@@ -1831,7 +1844,9 @@ hipError_t launch_gemm_dgrad_split(const GemmProblem &p, bool bf16_out, int spli
     const int ns = static_cast<int>((p.P + q.psplit - 1) / q.psplit);
     if (!big_offsets_fit(q))
         return launch_gemm_dgrad(p, bf16_out ? Epi::kStoreBF16 : Epi::kStoreF32, s);
-    const hipError_t e = launch_big<256, 256, 4, 2, true, false>(q, Epi::kStoreF32, 8, s);
+    const hipError_t e = p.C <= 128
+                             ? launch_big<256, 128, 4, 2, true, false>(q, Epi::kStoreF32, 8, s)
+                             : launch_big<256, 256, 4, 2, true, false>(q, Epi::kStoreF32, 8, s);
     if (e != hipSuccess)
         return e;
     const int64_t nthr = p.C * (R4 / 4);
