@@ -26,7 +26,8 @@ half of the metric.  Beside the step the same run measures:
   fraction, and the median FP32-output overhead;
 * the logits GEMM cold (L2 and MALL flushed between samples) and warm at
   M=128 K=4096 and M=1024 K=8192;
-* the full step at M=4096 K=16384 V=131072 (per-kernel times);
+* the full steps at M=4096 K=16384 V=131072 and M=128 K=4096 V=32768
+  (per-kernel times);
 * what the chip sustains: a register-only MFMA loop and a 1 GiB copy; and
   the vendor BLAS on the step's GEMM (BF16 out), for context;
 * the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
@@ -293,17 +294,20 @@ def vendor_context(torch, x, W, M, K, V, samples):
             "tflops": 2.0 * M * K * V / (med * 1e-3) / 1e12}
 
 
-def step_4096(torch, lmh, steps, seed):
-    """The full step at M=4096 K=16384 V=131072 (x ~ N(0,1), W ~ N(0, 0.01^2)
-    BF16 from torch's device generator, targets uniform, none ignored):
-    FP32 logits -> CE fwd -> mean -> CE bwd (BF16 dlogits) -> dgrad -> wgrad,
-    per-kernel HIP-event times (medians) over `steps` steps after one warmup."""
-    M, K, V = 4096, 16384, 131072
+def step_full(torch, lmh, steps, seed, M, K, V, w_sigma, ignore_frac):
+    """One whole step at (M, K, V) (x ~ N(0,1), W ~ N(0, w_sigma^2) BF16 from
+    torch's device generator, targets uniform with round(ignore_frac * M) rows
+    ignored): FP32 logits -> CE fwd -> mean -> CE bwd (BF16 dlogits) -> dgrad
+    -> wgrad, per-kernel HIP-event times (medians) over `steps` steps after
+    one warmup."""
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed + 5)
     x = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
-    W = (torch.randn(V, K, device="cuda", generator=gen) * 0.01).to(torch.bfloat16)
+    W = (torch.randn(V, K, device="cuda", generator=gen) * w_sigma).to(torch.bfloat16)
     tgt = torch.randint(0, V, (M,), device="cuda", generator=gen, dtype=torch.int32)
+    n_ign = int(round(ignore_frac * M))
+    if n_ign:
+        tgt[torch.randperm(M, device="cuda", generator=gen)[:n_ign]] = -100
     logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
     loss = torch.empty((M,), dtype=torch.float32, device="cuda")
     stats = torch.empty((M, 4), dtype=torch.float32, device="cuda")
@@ -333,15 +337,15 @@ def step_4096(torch, lmh, steps, seed):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     flop = 2.0 * M * K * V
-    res = {"workload": "M=4096 K=16384 V=131072 full step", "ms_per_step": 1e3 * wall,
-           "gemm_tflops_per_step": 3 * flop / wall / 1e12}
+    res = {"workload": f"M={M} K={K} V={V} full step, {n_ign} rows ignored",
+           "ms_per_step": 1e3 * wall, "gemm_tflops_per_step": 3 * flop / wall / 1e12}
     for name in ("logits", "xent_fwd", "xent_mean", "xent_bwd", "dgrad", "wgrad"):
         med = statistics.median(tm.ms(name))
         res[f"{name}_ms"] = med
         if name in ("logits", "dgrad", "wgrad"):
             res[f"{name}_tflops"] = flop / (med * 1e-3) / 1e12
-    n = M * V
-    res["ce_fwd_bwd_gbps"] = (4.0 * n + 24 * M + 4.0 * n + 2.0 * n + 24 * M) / (
+    n, nv = M * V, (M - n_ign) * V
+    res["ce_fwd_bwd_gbps"] = (4.0 * n + 24 * M + 4.0 * nv + 2.0 * n + 24 * M) / (
         (res["xent_fwd_ms"] + res["xent_bwd_ms"]) * 1e-3) / 1e9
     del x, W, tgt, logits, loss, stats, mean, inv, dlog, dX, dW, ws
     torch.cuda.empty_cache()
@@ -681,11 +685,19 @@ def main():
         out["logits_cold_vs_warm"] = cold_vs_warm(torch, lmh, args.samples, workloads.SEED)
     if not args.no_side and not args.no_grid:
         log("[bench] the full step at M=4096 K=16384 V=131072")
-        out["step_4096"] = step_4096(torch, lmh, 3, workloads.SEED)
+        out["step_4096"] = step_full(torch, lmh, 3, workloads.SEED, 4096, 16384, 131072, 0.01,
+                                     0.0)
         s4 = out["step_4096"]
         log(f"[bench]   {s4['ms_per_step']:.2f} ms per step; logits {s4['logits_tflops']:.0f}, "
             f"dgrad {s4['dgrad_tflops']:.0f}, wgrad {s4['wgrad_tflops']:.0f} TFLOPS; CE "
             f"{s4['ce_fwd_bwd_gbps']:.0f} GB/s")
+        log("[bench] the full step at M=128 K=4096 V=32768 (5 % rows ignored)")
+        out["step_128"] = step_full(torch, lmh, 20, workloads.SEED, 128, 4096, 32768, 0.02, 0.05)
+        s1 = out["step_128"]
+        log(f"[bench]   {s1['ms_per_step'] * 1e3:.1f} us per step; logits "
+            f"{s1['logits_ms'] * 1e3:.1f}, CE fwd {s1['xent_fwd_ms'] * 1e3:.1f}, bwd "
+            f"{s1['xent_bwd_ms'] * 1e3:.1f}, dgrad {s1['dgrad_ms'] * 1e3:.1f}, wgrad "
+            f"{s1['wgrad_ms'] * 1e3:.1f} us")
     if not args.no_side:
         log("[bench] sustained peaks: MFMA loop, device copy")
         out["sustained_peaks"] = sustained_peaks(torch, lmh)

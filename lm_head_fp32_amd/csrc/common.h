@@ -33,7 +33,48 @@ struct GemmProblem {
     // tile at D + y * split_stride.  psplit == 0: no split.
     int64_t psplit = 0;
     int64_t split_stride = 0;
+    // Output stores bypass the caches' normal allocation (nontemporal): a
+    // GEMM's output is written once and not read back by this kernel, and
+    // lines left dirty in L2 and the 256 MB MALL would otherwise be written
+    // back during the next kernel's reads.  Off for partial sums that the
+    // next kernel reads back at once.
+    bool stream_out = true;
 };
+
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store16(float *p, float4 v, bool stream)
+{
+    if (stream) {
+        const f32x4_nt w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4_nt *>(p));
+    } else {
+        *reinterpret_cast<float4 *>(p) = v;
+    }
+}
+
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store8(uint16_t *p, uint2 v, bool stream)
+{
+    if (stream) {
+        const u32x2_nt w = {v.x, v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_nt *>(p));
+    } else {
+        *reinterpret_cast<uint2 *>(p) = v;
+    }
+}
+
+__device__ __forceinline__ void store16(uint16_t *p, uint4 v, bool stream)
+{
+    if (stream) {
+        const u32x4_nt w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt *>(p));
+    } else {
+        *reinterpret_cast<uint4 *>(p) = v;
+    }
+}
 
 enum class Epi : int { kStoreF32 = 0, kStoreBF16 = 1, kAccumF32 = 2, kStoreF32Stats = 3 };
 

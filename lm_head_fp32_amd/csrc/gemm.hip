@@ -563,7 +563,8 @@ struct TrOperand {
 // fragment writes and the row reads below hit distinct banks.  Then every wave
 // reads whole rows and stores them with one 16-byte access per lane (the MFMA
 // result's register layout would store 32 bytes into each of 32 rows per
-// instruction).  EPI: FP32 store, FP32 accumulate (D += tile), or BF16 store
+// instruction; the stores are nontemporal unless g.stream_out is off).  EPI:
+// FP32 store, FP32 accumulate (D += tile), or BF16 store
 // (rounded to nearest-even in registers by v_cvt_pk_bf16_f32 and staged as
 // BF16, 8 values per lane and store).  Every thread of the workgroup must call
 // this.
@@ -628,7 +629,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&ac
                     const uint4 v = *reinterpret_cast<const uint4 *>(src);
                     uint16_t *out = static_cast<uint16_t *>(g.D) + c * g.ldd + r;
                     if (r + 8 <= g.R) {
-                        *reinterpret_cast<uint4 *>(out) = v;
+                        store16(out, v, g.stream_out);
                     } else {
                         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
                         for (int e = 0; e < 8 && r + e < g.R; ++e)
@@ -643,7 +644,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmProblem &g, f32x16 (&ac
                             const float4 o = *reinterpret_cast<const float4 *>(out);
                             w.x += o.x, w.y += o.y, w.z += o.z, w.w += o.w;
                         }
-                        *reinterpret_cast<float4 *>(out) = w;
+                        store16(out, w, g.stream_out);
                     } else {
                         const float vv[4] = {v.x, v.y, v.z, v.w};
                         for (int e = 0; e < 4 && r + e < g.R; ++e) {
@@ -1501,7 +1502,7 @@ gemm_rows(GemmProblem g, int groups_per_wg)
                     const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
                     const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
                     if (r + 4 <= g.R) {
-                        *reinterpret_cast<uint2 *>(out) = make_uint2(w0, w1);
+                        store8(out, make_uint2(w0, w1), g.stream_out);
                     } else {
                         const uint32_t ww[2] = {w0, w1};
                         for (int e = 0; e < 4 && r + e < g.R; ++e)
@@ -1510,7 +1511,7 @@ gemm_rows(GemmProblem g, int groups_per_wg)
                 } else {
                     float *out = static_cast<float *>(g.D) + c * g.ldd + r;
                     if (r + 4 <= g.R) {
-                        *reinterpret_cast<float4 *>(out) = sum;
+                        store16(out, sum, g.stream_out);
                     } else {
                         for (int e = 0; e < 4 && r + e < g.R; ++e)
                             out[e] = vv[e];
@@ -1797,7 +1798,7 @@ __global__ void __launch_bounds__(256) splitk_reduce(const float *ws, int S, int
         const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
         const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
         if (r + 4 <= R) {
-            *reinterpret_cast<uint2 *>(out) = make_uint2(w0, w1);
+            store8(out, make_uint2(w0, w1), true);
         } else {
             const uint32_t w[2] = {w0, w1};
             for (int e = 0; e < 4 && r + e < R; ++e)
@@ -1806,7 +1807,7 @@ __global__ void __launch_bounds__(256) splitk_reduce(const float *ws, int S, int
     } else {
         float *out = static_cast<float *>(D) + c * ldd + r;
         if (r + 4 <= R) {
-            *reinterpret_cast<float4 *>(out) = a;
+            store16(out, a, true);
         } else {
             for (int e = 0; e < 4 && r + e < R; ++e)
                 out[e] = v[e];
@@ -1841,6 +1842,7 @@ hipError_t launch_gemm_dgrad_split(const GemmProblem &p, bool bf16_out, int spli
     q.split_stride = p.C * R4;
     q.D = ws;
     q.ldd = R4;
+    q.stream_out = false;  // read back at once by splitk_reduce
     const int ns = static_cast<int>((p.P + q.psplit - 1) / q.psplit);
     if (!big_offsets_fit(q))
         return launch_gemm_dgrad(p, bf16_out ? Epi::kStoreBF16 : Epi::kStoreF32, s);
