@@ -26,8 +26,8 @@ half of the metric.  Beside the step the same run measures:
   fraction, and the median FP32-output overhead;
 * the logits GEMM cold (L2 and MALL flushed between samples) and warm at
   M=128 K=4096 and M=1024 K=8192;
-* the full steps at M=4096 K=16384 V=131072 and M=128 K=4096 V=32768
-  (per-kernel times);
+* the full steps at M=4096 K=16384 V=131072, at one GPU's token shard of it
+  (M=512), and at M=128 K=4096 V=32768 (per-kernel times);
 * what the chip sustains: a register-only MFMA loop and a 1 GiB copy; and
   the vendor BLAS on the step's GEMM (BF16 out), for context;
 * the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
@@ -691,6 +691,12 @@ def main():
         log(f"[bench]   {s4['ms_per_step']:.2f} ms per step; logits {s4['logits_tflops']:.0f}, "
             f"dgrad {s4['dgrad_tflops']:.0f}, wgrad {s4['wgrad_tflops']:.0f} TFLOPS; CE "
             f"{s4['ce_fwd_bwd_gbps']:.0f} GB/s")
+        log("[bench] one GPU's token shard of that step (M=512 of 4096, eight GPUs)")
+        out["step_4096_token_shard_of_8"] = step_full(torch, lmh, 3, workloads.SEED, 512, 16384,
+                                                      131072, 0.01, 0.0)
+        s8 = out["step_4096_token_shard_of_8"]
+        log(f"[bench]   {s8['ms_per_step']:.2f} ms per step; logits {s8['logits_tflops']:.0f}, "
+            f"dgrad {s8['dgrad_tflops']:.0f}, wgrad {s8['wgrad_tflops']:.0f} TFLOPS")
         log("[bench] the full step at M=128 K=4096 V=32768 (5 % rows ignored)")
         out["step_128"] = step_full(torch, lmh, 20, workloads.SEED, 128, 4096, 32768, 0.02, 0.05)
         s1 = out["step_128"]
