@@ -326,6 +326,27 @@ def test_wgrad_integer_exact_and_accumulate(M, K, V):
     assert np.array_equal(_f32_bits(host_f32(dw)), _f32_bits((2 * ref).astype(np.float32)))
 
 
+def test_wgrad_pipelined_integer_exact():
+    """wgrad with enough tiles for the pipelined persistent kernel (each tile's
+    FP32 results stored during the next tile's stages), ragged in K and V
+    (edge tiles both ways), into a NaN-filled padded dW: no element left
+    unwritten, padding untouched, and bit-exact rows at both V edges and in
+    between against the oracle."""
+    M, K, V = 96, 4100, 16500
+    dl_bits, x_bits = workloads.integer_operands([(M, V), (M, K)], seed=77)
+    _say(f"wgrad pipelined int M={M} K={K} V={V}")
+    dl, x = dev_bf16(dl_bits, _up(V, 8)), dev_bf16(x_bits, _up(K, 8))
+    dw = padded_out(V, K, _up(K, 4) + 4, torch.float32)
+    lmh.lmhead_wgrad(dl, x, dW=dw)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dw).any().item()
+    assert padding_untouched(dw)
+    rows = np.concatenate([np.arange(0, 130), np.arange(8190, 8200), np.arange(16380, V)])
+    ref, _ = oracle.wgrad(dl_bits, x_bits, rows=rows)
+    assert np.array_equal(_f32_bits(host_f32(dw[torch.from_numpy(rows).cuda()])),
+                          _f32_bits(ref.astype(np.float32)))
+
+
 def test_wgrad_random_sampled():
     """dW = dl^T . x at M=1024, K=8192, V=32768 with synthetic BF16 dl."""
     rng = np.random.default_rng(workloads.SEED + 4)
