@@ -281,15 +281,14 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
  *
  *  When M x K has too few 256 x 256 output tiles to fill the chip (fewer than
  *  256, e.g. M = 1024, K = 8192, or few tokens), the V sum is split `splits`
- *  ways; every
- *  split writes an FP32 partial dX into `workspace`, and a second kernel adds
- *  the partials in split order and stores dX (FP32, or BF16 rounded to
- *  nearest-even once, from the FP32 sum).  splits == 0 picks the shape's
- *  default (1 - 16 parts, for ~256 workgroups); 1 <= splits <= 16 asks for
- *  that many parts of whole
- *  64-deep stages (fewer when V is small).  The result is deterministic run to
- *  run; its summation order differs from lmhead_dgrad's, so the two agree
- *  within the FP32 tolerance, and bitwise on integer inputs.
+ *  ways; every part writes an FP32 partial dX into `workspace`, and a second
+ *  kernel adds the partials in split order and stores dX (FP32, or BF16
+ *  rounded to nearest-even once, from the FP32 sum).  splits == 0 picks the
+ *  shape's default (1 - 16 parts, for ~256 workgroups); 1 <= splits <= 16
+ *  asks for that many parts of whole 64-deep stages (fewer when V is small).
+ *  The result is deterministic run to run; its summation order differs from
+ *  lmhead_dgrad's, so the two agree within the FP32 tolerance, and bitwise on
+ *  integer inputs.
  *
  *  lmhead_dgrad_workspace_bytes returns the workspace bytes that
  *  lmhead_dgrad_ws needs for (M, K, V, splits): parts x M x K4 x 4 with K4 =
