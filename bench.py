@@ -244,20 +244,25 @@ def cold_vs_warm(torch, lmh, samples, seed):
 
 def sustained_peaks(torch, lmh):
     """What the chip sustains: a register-only MFMA loop (the library's
-    diagnostic kernel, two waves per SIMD) and a 1 GiB device copy."""
+    diagnostic kernel, two waves per SIMD) on all-ones operands (almost no
+    bit switching) and on pseudo-random operands (switching like real data),
+    and a 1 GiB device copy."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n_wg, iters = 2 * cus, 20000
     sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        lmh.lmhead_diag_mfma_loop(iters, n_wg, sink)
     tm = KernelTimer(torch)
-    for _ in range(5):
-        tm("mfma", lambda: lmh.lmhead_diag_mfma_loop(iters, n_wg, sink))
-    torch.cuda.synchronize()
-    if not torch.all(sink == 128.0 * iters).item():
-        raise RuntimeError("MFMA loop diagnostic returned a wrong closed-form value")
-    t_mfma = statistics.median(tm.ms("mfma"))
-    mfma_tflops = n_wg * lmh.MFMA_LOOP_FLOP_PER_WORKGROUP_ITER * iters / (t_mfma * 1e-3) / 1e12
+    for kind in ("ones", "random"):
+        for _ in range(2):
+            lmh.lmhead_diag_mfma_loop(iters, n_wg, sink, operands=kind)
+        for _ in range(5):
+            tm(kind, lambda: lmh.lmhead_diag_mfma_loop(iters, n_wg, sink, operands=kind))
+        torch.cuda.synchronize()
+        want = 128.0 * iters if kind == "ones" else 0.0
+        if not torch.all(sink == want).item():
+            raise RuntimeError(f"MFMA loop diagnostic ({kind}) returned a wrong closed-form value")
+    flop = n_wg * lmh.MFMA_LOOP_FLOP_PER_WORKGROUP_ITER * iters
+    mfma_tflops = flop / (statistics.median(tm.ms("ones")) * 1e-3) / 1e12
+    mfma_rand_tflops = flop / (statistics.median(tm.ms("random")) * 1e-3) / 1e12
     nb = 1 << 30
     src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -270,8 +275,11 @@ def sustained_peaks(torch, lmh):
     del src, dst, sink
     return {"mfma_bf16_loop_tflops": mfma_tflops,
             "mfma_bf16_loop_frac_of_peak": mfma_tflops / PEAK_BF16_TFLOPS,
+            "mfma_bf16_loop_random_tflops": mfma_rand_tflops,
+            "mfma_bf16_loop_random_frac_of_peak": mfma_rand_tflops / PEAK_BF16_TFLOPS,
             "mfma_loop": f"{n_wg} workgroups x 4 waves x 8 chains x {iters} 32x32x16 MFMAs, "
-                         "register operands only",
+                         "register operands only; all ones, then pseudo-random BF16 "
+                         "(random sign and mantissa)",
             "copy_gbps": 2.0 * nb / (t_copy * 1e-3) / 1e9,
             "copy_frac_of_peak": 2.0 * nb / (t_copy * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "copy": "1 GiB device-to-device copy, read + write bytes"}
@@ -708,7 +716,12 @@ def main():
         log("[bench] sustained peaks: MFMA loop, device copy")
         out["sustained_peaks"] = sustained_peaks(torch, lmh)
         sp = out["sustained_peaks"]
-        log(f"[bench]   MFMA loop {sp['mfma_bf16_loop_tflops']:.0f} TFLOPS, copy "
+        out["roofline"]["sustained_random_operand_tflops"] = round(
+            sp["mfma_bf16_loop_random_tflops"], 2)
+        out["roofline"]["frac_of_sustained_random"] = round(
+            logits_tflops / sp["mfma_bf16_loop_random_tflops"], 4)
+        log(f"[bench]   MFMA loop {sp['mfma_bf16_loop_tflops']:.0f} TFLOPS (all-ones operands), "
+            f"{sp['mfma_bf16_loop_random_tflops']:.0f} TFLOPS (random operands), copy "
             f"{sp['copy_gbps']:.0f} GB/s")
         out["vendor_gemm_context"] = vendor_context(torch, x, W, M, K, V, args.samples)
         log(f"[bench]   vendor BLAS (bf16 out) {out['vendor_gemm_context']['tflops']:.0f} TFLOPS")

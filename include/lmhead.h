@@ -329,15 +329,26 @@ int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ld
  *  beside the GEMMs so their throughput can be compared with what the chip
  *  sustains under full matrix load at its power limit (the datasheet peak
  *  assumes 2.4 GHz).  n_workgroups workgroups of 256 threads (4 waves) each
- *  run 8 independent chains of `iters` 32x32x16 BF16 MFMAs with all operands
- *  1.0: 2 * 32 * 32 * 16 * 8 * iters FLOP per wave, 4 waves per workgroup.
- *  sink FP32 [n_workgroups * 256] receives, per thread, 128 * iters exactly
- *  (the sum of element 0 of its 8 accumulators), which checks that every
- *  MFMA ran.  Limits: 0 <= iters, 128 * iters < 2^24 (exact in FP32) and
+ *  run 8 independent chains of `iters` 32x32x16 BF16 MFMAs:
+ *  2 * 32 * 32 * 16 * 8 * iters FLOP per wave, 4 waves per workgroup.
+ *  operands selects the data, which sets how much the multipliers switch and
+ *  so the power drawn:
+ *    0  every operand 1.0.  sink FP32 [n_workgroups * 256] receives, per
+ *       thread, 128 * iters exactly (the sum of element 0 of its 8
+ *       accumulators), which checks that every MFMA ran.
+ *    1  pseudo-random BF16 operands (random sign and 7 mantissa bits, |v| in
+ *       [1, 2), a different set per lane) cycling through (A1, B1), (A2, B2),
+ *       (A1, -B1), (A2, -B2), so every accumulator returns to exactly 0 each
+ *       fourth MFMA of its chain (all partial sums are exact in FP32).  sink
+ *       receives, per thread, element 0 of its 8 accumulators weighted
+ *       1 ... 8: 0 when iters % 4 == 0, and for other iters a value that
+ *       depends only on iters % 4.
+ *  Limits: operands in {0, 1}, 0 <= iters, 128 * iters < 2^24 and
  *  0 <= n_workgroups <= 65536, else LMH_ERR_SHAPE; n_workgroups == 0 is a
  *  no-op.  sink must not be NULL (LMH_ERR_NULL) and 16-byte aligned.
  */
-int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, float *sink, void *stream);
+int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, int32_t operands,
+                              float *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,7 @@ _SIGNATURES = {
                          _vp], _i32),
     "lmhead_dgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
     "lmhead_wgrad": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _vp], _i32),
-    "lmhead_diag_mfma_loop": ([_i64, _i64, _vp, _vp], _i32),
+    "lmhead_diag_mfma_loop": ([_i64, _i64, _i32, _vp, _vp], _i32),
     "lmhead_dgrad_workspace_bytes": ([_i64, _i64, _i64, _i32], _i64),
     "lmhead_dgrad_ws": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
                          _vp], _i32),
@@ -452,14 +452,19 @@ def lmhead_wgrad(dlogits, x, dW=None, accumulate=False, stream=None):
 MFMA_LOOP_FLOP_PER_WORKGROUP_ITER = 2 * 32 * 32 * 16 * 8 * 4  # 8 chains x 4 waves
 
 
-def lmhead_diag_mfma_loop(iters, n_workgroups, sink=None, stream=None):
+def lmhead_diag_mfma_loop(iters, n_workgroups, sink=None, stream=None, operands="ones"):
     """Diagnostic register-only MFMA loop; returns sink [n_workgroups * 256]
-    FP32, every element 128 * iters when every MFMA ran."""
+    FP32.  operands="ones": every element 128 * iters when every MFMA ran;
+    operands="random": pseudo-random operands whose sums cancel exactly,
+    every element 0 when iters % 4 == 0."""
     iters, n_workgroups = int(iters), int(n_workgroups)
+    if operands not in ("ones", "random"):
+        raise ValueError("operands must be 'ones' or 'random'")
     if sink is None:
         sink = torch.empty(max(n_workgroups, 0) * 256, dtype=torch.float32, device="cuda")
     if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < n_workgroups * 256:
         raise ValueError("sink must be a contiguous fp32 tensor of n_workgroups * 256 elements")
-    _check("lmhead_diag_mfma_loop", lib().lmhead_diag_mfma_loop(iters, n_workgroups,
-                                                                sink.data_ptr(), _stream(stream)))
+    _check("lmhead_diag_mfma_loop",
+           lib().lmhead_diag_mfma_loop(iters, n_workgroups, 1 if operands == "random" else 0,
+                                       sink.data_ptr(), _stream(stream)))
     return sink

@@ -497,9 +497,12 @@ int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ld
         static_cast<hipStream_t>(stream)));
 }
 
-int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, float *sink, void *stream)
+int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, int32_t operands, float *sink,
+                              void *stream)
 {
     const int64_t chains = lmh::mfma_loop_chains();
+    if (operands != 0 && operands != 1)
+        return LMH_ERR_SHAPE;
     if (iters < 0 || n_workgroups < 0 || n_workgroups > kMaxDiagWorkgroups ||
         16 * chains * iters >= (int64_t{1} << 24))
         return LMH_ERR_SHAPE;
@@ -509,7 +512,7 @@ int32_t lmhead_diag_mfma_loop(int64_t iters, int64_t n_workgroups, float *sink, 
         return LMH_ERR_NULL;
     if (!aligned16(sink))
         return LMH_ERR_ALIGN;
-    return launch_status(lmh::launch_mfma_loop(iters, n_workgroups, sink,
+    return launch_status(lmh::launch_mfma_loop(iters, n_workgroups, operands == 1, sink,
                                                static_cast<hipStream_t>(stream)));
 }
 

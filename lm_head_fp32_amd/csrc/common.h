@@ -114,9 +114,10 @@ hipError_t launch_xent_bwd(const float *logits, int64_t ld, const float *stats,
                            int64_t dloss_stride, void *dlogits, int64_t ldg, bool bf16_out,
                            int64_t n_rows, int64_t n_cols, hipStream_t s);
 // Register-only MFMA loop (diagnostic): 256-thread workgroups, one float per
-// thread written to sink.
+// thread written to sink; all-ones or pseudo-random operands.
 int mfma_loop_chains();
-hipError_t launch_mfma_loop(int64_t iters, int64_t n_workgroups, float *sink, hipStream_t s);
+hipError_t launch_mfma_loop(int64_t iters, int64_t n_workgroups, bool random_operands,
+                            float *sink, hipStream_t s);
 
 // exp(z - m) as one hardware base-2 exponential; the same form everywhere the
 // cross-entropy statistics are computed (CE kernels, logits GEMM epilogue).

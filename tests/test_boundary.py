@@ -269,13 +269,16 @@ def test_dgrad_workspace_and_split_validation(L):
 
 def test_diag_mfma_loop_validation(L):
     f = L.lmhead_diag_mfma_loop
-    assert f(-1, 4, A, None) == SHAPE
-    assert f(1 << 17, 4, A, None) == SHAPE           # 128 * iters must stay below 2^24
-    assert f(10, -1, A, None) == SHAPE
-    assert f(10, 65537, A, None) == SHAPE
-    assert f(10, 4, None, None) == NULL
-    assert f(10, 4, A + 4, None) == ALIGN
-    assert f(10, 0, None, None) == OK                # no workgroups: no-op
+    for mode in (0, 1):
+        assert f(-1, 4, mode, A, None) == SHAPE
+        assert f(1 << 17, 4, mode, A, None) == SHAPE     # 128 * iters must stay below 2^24
+        assert f(10, -1, mode, A, None) == SHAPE
+        assert f(10, 65537, mode, A, None) == SHAPE
+        assert f(10, 4, mode, None, None) == NULL
+        assert f(10, 4, mode, A + 4, None) == ALIGN
+        assert f(10, 0, mode, None, None) == OK          # no workgroups: no-op
+    assert f(10, 4, 2, A, None) == SHAPE                 # operand kind outside {0, 1}
+    assert f(10, 4, -1, A, None) == SHAPE
 
 
 def test_binding_rejects_cpu_tensors():
