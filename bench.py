@@ -28,7 +28,8 @@ half of the metric.  Beside the step the same run measures:
   M=128 K=4096 and M=1024 K=8192;
 * the full steps at M=4096 K=16384 V=131072, at one GPU's token shard of it
   (M=512), and at M=128 K=4096 V=32768 (per-kernel times);
-* what the chip sustains: a register-only MFMA loop and a 1 GiB copy; and
+* what the chip sustains: a register-only MFMA loop (all-ones and
+  pseudo-random operands) and a 1 GiB copy; and
   the vendor BLAS on the step's GEMM (BF16 out), for context;
 * the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
 
@@ -56,9 +57,9 @@ PEAK_HBM_GBS = 8000.0
 # counters on this GPU), valid only for the kernel sources they were taken on
 # (code hash of the .hip file, see source_code_hash).  Changed code reports null.
 MEASURED_TRAFFIC = {
-    "logits_fp32": {"src": "gemm.hip", "sha": "9faeaefd48a9b9ea", "bytes": (2 * 395648 + 131092) * 1024},
+    "logits_fp32": {"src": "gemm.hip", "sha": "9faeaefd48a9b9ea", "bytes": (2 * 395862 + 131101) * 1024},
     "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "90e3a3bef99ccf2c",
-                          "bytes": (2 * 2097954 + 514 + 2 * 2056476 + 4195628) * 1024},
+                          "bytes": (2 * 2097954 + 514 + 2 * 2056476 + 4195334) * 1024},
 }
 
 
