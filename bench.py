@@ -29,8 +29,9 @@ half of the metric.  Beside the step the same run measures:
 * the full steps at M=4096 K=16384 V=131072, at one GPU's token shard of it
   (M=512), and at M=128 K=4096 V=32768 (per-kernel times);
 * what the chip sustains: a register-only MFMA loop (all-ones and
-  pseudo-random operands) and a 1 GiB copy; and
-  the vendor BLAS on the step's GEMM (BF16 out), for context;
+  pseudo-random operands) and a 1 GiB copy; board power and clock (amdsmi
+  sensors) while the logits GEMM and the MFMA loops run; and the vendor BLAS
+  on the step's GEMM (BF16 out), for context;
 * the FP64 CPU oracle on a bounded sample of the same work (cpu_baseline).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -284,6 +285,51 @@ def sustained_peaks(torch, lmh):
             "copy_gbps": 2.0 * nb / (t_copy * 1e-3) / 1e9,
             "copy_frac_of_peak": 2.0 * nb / (t_copy * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "copy": "1 GiB device-to-device copy, read + write bytes"}
+
+
+def power_under_load(torch, fn, flop, seconds=3.0):
+    """Board power (W) and graphics clock (MHz) sampled from the device's
+    sensors (amdsmi, through torch.cuda) while fn runs back to back, after a
+    one-second settle; with the achieved TFLOPS of that run.  None where the
+    sensors cannot be read."""
+    try:
+        torch.cuda.power_draw()
+        torch.cuda.clock_rate()
+    except Exception:  # no sensor access: report nothing rather than guess
+        return None
+    fn()
+    torch.cuda.synchronize()
+    pw, ck = [], []
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        if time.time() - t0 > 1.0:
+            pw.append(float(torch.cuda.power_draw()))
+            ck.append(float(torch.cuda.clock_rate()))
+        if n % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    dt = time.time() - t0
+    if not pw:
+        return None
+    return {"power_w": statistics.median(pw), "clock_mhz": statistics.median(ck),
+            "samples": len(pw), "tflops": flop * n / dt / 1e12}
+
+
+def power_cap_w(torch):
+    """The board's power cap in W (amdsmi), or None."""
+    try:
+        import amdsmi
+
+        handle = torch.cuda._get_amdsmi_handler(0)
+        cap = amdsmi.amdsmi_get_power_cap_info(handle)["power_cap"]
+        cap = float(cap)
+        return cap / 1e6 if cap > 1e5 else cap  # the library reports microwatts
+    except Exception:
+        return None
 
 
 def vendor_context(torch, x, W, M, K, V, samples):
@@ -724,6 +770,27 @@ def main():
         log(f"[bench]   MFMA loop {sp['mfma_bf16_loop_tflops']:.0f} TFLOPS (all-ones operands), "
             f"{sp['mfma_bf16_loop_random_tflops']:.0f} TFLOPS (random operands), copy "
             f"{sp['copy_gbps']:.0f} GB/s")
+        log("[bench] board power and clock under load (logits GEMM, MFMA loops)")
+        n_wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+        psink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+        loop_flop = n_wg * lmh.MFMA_LOOP_FLOP_PER_WORKGROUP_ITER * 2000
+        out["power"] = {
+            "cap_w": power_cap_w(torch),
+            "logits_gemm_fp32": power_under_load(
+                torch, lambda: lmh.lmhead_logits(x, W, out=logits, out_dtype="fp32"),
+                2.0 * M * K * V),
+            "mfma_loop_random": power_under_load(
+                torch, lambda: lmh.lmhead_diag_mfma_loop(2000, n_wg, psink, operands="random"),
+                loop_flop),
+            "mfma_loop_ones": power_under_load(
+                torch, lambda: lmh.lmhead_diag_mfma_loop(2000, n_wg, psink, operands="ones"),
+                loop_flop),
+        }
+        del psink
+        pl = out["power"]["logits_gemm_fp32"]
+        if pl:
+            log(f"[bench]   cap {out['power']['cap_w']} W; logits GEMM {pl['power_w']:.0f} W at "
+                f"{pl['clock_mhz']:.0f} MHz, {pl['tflops']:.0f} TFLOPS")
         out["vendor_gemm_context"] = vendor_context(torch, x, W, M, K, V, args.samples)
         log(f"[bench]   vendor BLAS (bf16 out) {out['vendor_gemm_context']['tflops']:.0f} TFLOPS")
 
