@@ -20,9 +20,17 @@ kinds and checks the claims it rests on:
                                 on the FP64 logits rounded to FP32: the BF16
                                 logits' loss error is >= 10x the FP32 logits'.
 
-The legacy BF16-arithmetic backward of the old fused CE kernel is not
-rebuilt here; both logit kinds feed the FP32 backward.  Run with -s to see
-the table."""
+Both logit kinds feed the FP32 backward in that table.  A second table
+(test_precision_study_bf16_backward) sets the FP32 backward against the old
+fused kernel's BF16 backward as Transformer Engine issue "[Pytorch] change
+fused cross entropy backward grad to fp32 ..." describes it ("Description":
+the backward ran in BF16 for BF16 input; discussion: the gradients were
+stored over the BF16 input): softmax minus one-hot stored in BF16, then
+scaled by the upstream gradient in BF16.  Checked claims: the FP32 backward
+keeps each gradient row summing to zero; the BF16 one is within half a BF16
+ulp of it elementwise, >= 100x further from the FP64 gradient, and its rows
+no longer sum to zero (the target entry -(1 - p_y) rounds to -1).  Run with
+-s to see the tables."""
 import numpy as np
 import pytest
 import torch
@@ -117,3 +125,54 @@ def test_precision_study_normal_operands():
         assert r["loss_err_f32"] <= 1e-5 * max(1.0, r["logit_scale"])
         assert r["loss_err_bf16"] >= 10.0 * max(r["loss_err_f32"], 1e-7)
         assert r["grad_err_f32"] <= 1e-6
+
+
+def _old_style_grad(z32_dev, t_dev, dl):
+    """The old kernel's gradient: softmax - one-hot from lmhead_xent_bwd with
+    unit upstream gradient, stored in BF16 (its BF16 output), then scaled by
+    the upstream gradient in BF16 arithmetic -- the exact product of two BF16
+    values rounded to nearest-even BF16 by the oracle's rounding helper."""
+    _, st = lmh.lmhead_xent_fwd(z32_dev, t_dev)
+    g = lmh.lmhead_xent_bwd(z32_dev, st, t_dev, torch.ones(1, device="cuda"), grad_dtype="bf16")
+    torch.cuda.synchronize()
+    g16 = oracle.bf16_bits_to_f64(host_bits(g))
+    dl16 = oracle.bf16_bits_to_f64(oracle.round_bf16(np.array([dl])))[0]
+    return oracle.bf16_bits_to_f64(oracle.round_bf16(g16 * dl16))
+
+
+def _grad_metrics(g, gref):
+    err = np.abs(g - gref)
+    rel = np.linalg.norm(g - gref, axis=1) / np.linalg.norm(gref, axis=1)
+    return float(err.max()), float(np.median(rel)), float(np.abs(g.sum(axis=1)).max())
+
+
+@pytest.mark.parametrize("K", (512, 4096, 16384))
+def test_precision_study_bf16_backward(K):
+    inp = workloads.normal_gemm(M, K, V, 0.02, seed=workloads.SEED + K)
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    l32 = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    l16 = lmh.lmhead_logits(x, W, out_dtype="bf16")
+    torch.cuda.synchronize()
+    exact, _ = oracle.logits(inp.x, inp.W)
+    t = dev_i32(inp.target)
+    dl = 1.0 / M
+    gref = oracle.xent_bwd(exact.astype(np.float32), inp.target, -100, dl)
+    _, g_new = _ce(l32, t, dl)                                   # FP32 logits, FP32 backward
+    g_old_bwd = _old_style_grad(l32, t, dl)                       # FP32 logits, BF16 backward
+    b16 = oracle.bf16_bits_to_f64(host_bits(l16)).astype(np.float32)
+    g_old = _old_style_grad(dev_f32(b16), t, dl)                  # BF16 logits, BF16 backward
+    rows = {"fp32 logits + fp32 bwd": _grad_metrics(g_new, gref),
+            "fp32 logits + bf16 bwd": _grad_metrics(g_old_bwd, gref),
+            "bf16 logits + bf16 bwd": _grad_metrics(g_old, gref)}
+    print(f"\nK={K}: path | max |err| | median row rel L2 err | max |row sum|  (dloss = {dl})")
+    for k, (mx, rel, rs) in rows.items():
+        print(f"  {k} | {mx:.3g} | {rel:.3g} | {rs:.3g}")
+    new, old = rows["fp32 logits + fp32 bwd"], rows["fp32 logits + bf16 bwd"]
+    assert new[0] <= 1e-6                                        # the FP32 gradient bar
+    assert new[2] <= 1e-5 * dl                                   # rows sum to zero
+    # BF16 storage of softmax - one-hot: at most half an ulp, 2^-8 relative
+    # (8-bit significand); dl is a power of two, so the BF16 scaling adds no
+    # rounding
+    assert np.all(np.abs(g_old_bwd - g_new) <= 2.0 ** -8 * np.abs(g_new) * (1 + 1e-6) + 1e-30)
+    assert old[1] >= 100.0 * max(new[1], 1e-12)
+    assert old[2] >= 100.0 * max(new[2], 1e-15)
