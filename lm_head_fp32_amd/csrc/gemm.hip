@@ -1718,13 +1718,20 @@ hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
     case 4: return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
     default: break;
     }
+    // wgrad's tile order (tile rows along K walked before stepping along V):
+    // with few tokens it is bound by its FP32 dW stores, and walking 16 tile
+    // rows -- whole 4096-wide dW row blocks -- writes longer runs of each row.
+    // Measured on MI355X against 8: M=128 K=4096 V=32768 -4 %, K=16384 -14 %,
+    // M=256 K=16384 -10 %, M=16 K=8192 -7 %; at M=512 K=16384 V=131072 16 was
+    // 6 % slower and at M=1024 K=8192 equal, so 8 above 256 tokens.
 #ifndef LMH_WGRAD_GROUP
-#define LMH_WGRAD_GROUP 8
+#define LMH_WGRAD_GROUP 0
 #endif
+    const int wgrad_group = LMH_WGRAD_GROUP > 0 ? LMH_WGRAD_GROUP : (p.P <= 256 ? 16 : 8);
     const int64_t tiles256 = ((p.R + 255) / 256) * ((p.C + 255) / 256);
     const int64_t tiles256x128 = ((p.R + 255) / 256) * ((p.C + 127) / 128);
     if (tiles256 >= 256)
-        return launch_big<256, 256, 4, 2, AT, BT>(p, epi, BT ? LMH_WGRAD_GROUP : 8, s);
+        return launch_big<256, 256, 4, 2, AT, BT>(p, epi, BT ? wgrad_group : 8, s);
     if (tiles256x128 >= 192)
         return launch_big<256, 128, 4, 2, AT, BT>(p, epi, 8, s);
     return launch_big<128, 128, 2, 2, AT, BT>(p, epi, 8, s);
