@@ -122,6 +122,34 @@ def integer_operands(shapes, seed: int = SEED, lo: int = -8, hi: int = 8):
     return [int_to_bf16_bits(rng.integers(lo, hi + 1, tuple(s))) for s in shapes]
 
 
+def random_shapes(n: int, seed: int, m_set, v_set, k8_max: int):
+    """n random problem shapes for parity sweeps, one generator, drawn in this
+    order per case: M from m_set, K = 8 * U[1, k8_max), V from v_set, then the
+    extra leading-dimension padding of x, W (multiples of 8 elements, 0 - 16),
+    of a BF16 [M, V] operand (0 or 8) and of an FP32 [M, V] operand (0 or 4)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice(m_set))
+        K = int(8 * rng.integers(1, k8_max))
+        V = int(rng.choice(v_set))
+        out.append({"M": M, "K": K, "V": V,
+                    "pad_x": int(8 * rng.integers(0, 3)), "pad_w": int(8 * rng.integers(0, 3)),
+                    "pad_g": int(8 * rng.integers(0, 2)), "pad_z": int(4 * rng.integers(0, 2))})
+    return out
+
+
+def uniform_targets(n: int, V: int, ignore_frac: float, seed: int) -> np.ndarray:
+    """Targets uniform in [0, V), then round(ignore_frac * n) rows set to the
+    ignore index (chosen without replacement)."""
+    rng = np.random.default_rng(seed)
+    t = rng.integers(0, V, n).astype(np.int32)
+    k = int(round(ignore_frac * n))
+    if k:
+        t[rng.choice(n, k, replace=False)] = IGNORE_INDEX
+    return t
+
+
 def tiny_exact(seed: int = SEED) -> GemmInputs:
     """x [16 x 512], W [1024 x 512] integers in [-8, 8], targets in [0, 1024)."""
     g = integer_gemm(16, 512, 1024, seed)
