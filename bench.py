@@ -96,6 +96,8 @@ def parse():
     ap.add_argument("--ce-rows", type=int, default=8192, help="rows of the large CE workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the side measurements")
+    ap.add_argument("--grid-only", action="store_true",
+                    help="run only the pages' 15-shape GEMM grid and print its JSON (profiling aid)")
     ap.add_argument("--no-grid", action="store_true",
                     help="skip the GEMM grid and the cold/warm measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -431,6 +433,11 @@ def main():
     lmh.lib()
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
+    if args.grid_only:
+        log("[bench] the pages' GEMM grid only")
+        print(json.dumps({"gemm_grid_fp32_vs_bf16": gemm_grid(torch, lmh, args.samples,
+                                                              workloads.SEED)}), flush=True)
+        return 0
 
     # ------------------------------------------------------------ the step
     M, K, V = 1024, 8192, 32768
