@@ -1586,6 +1586,110 @@ hipError_t launch_pp(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// gemm_wg2: wgrad for few tokens, two workgroups per CU.  With M <= 256 the
+// weight gradient is bound by its FP32 dW stores: a 256 x 256 tile computes
+// for a few microseconds and then stores 256 KiB, and with gemm_big's 128 KiB
+// of LDS a CU holds one workgroup, so its stores and the next tile's loads and
+// MFMAs take turns.  Here a tile is 256 (K) x 128 (V), four waves of 128 x 64
+// (128 accumulators per lane), and the contraction over tokens runs through a
+// single 64-deep LDS stage (A [64][256] + B [64][128], 48 KiB) inside a 64 KiB
+// area that the epilogue reuses for its two staging buffers; two workgroups
+// fit on a CU, so one's stores overlap the other's loads and MFMAs.  Both
+// operands are p-major (x [M][K], dlogits [M][V]) and go through the
+// transposing LDS reads of TrOperand; edge tiles and a ragged last stage use
+// its guarded register path.
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_wg2(GemmProblem g, TileMap tm)
+{
+    constexpr int BR = 256, BC = 128, BK = 64, WR = 2, WC = 2, NW = 4, NT = 256;
+    constexpr int TR = BR / WR, TC = BC / WC, FR = TR / 32, FC = TC / 32;
+    using OpA = TrOperand<BR, BK, NW>;
+    using OpB = TrOperand<BC, BK, NW>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 32 * BR * 2];  // 64 KiB
+    uint16_t *const sA = lds;                  // [BK][BR]
+    uint16_t *const sB = lds + BK * BR;        // [BK][BC]
+    static_assert(BK * BR + BK * BC <= 2 * 32 * BR * 2, "stage inside the staging area");
+
+    int tr, tc;
+    map_tile(tm, tr, tc);
+    const int64_t r0 = static_cast<int64_t>(tr) * BR;
+    const int64_t c0 = static_cast<int64_t>(tc) * BC;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % WR;
+    const int wc = wave / WR;
+    const bool interior = r0 + BR <= g.R && c0 + BC <= g.C;
+
+    OpA opA;
+    OpB opB;
+    opA.init(g.A, g.lda, r0, g.R, g.P, wave, lane, wr * TR);
+    opB.init(g.B, g.ldb, c0, g.C, g.P, wave, lane, wc * TC);
+
+    f32x16 acc[FR][FC];
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FC; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.0f;
+
+    const int64_t nk = (g.P + BK - 1) / BK;
+    const int64_t nfull = g.P / BK;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        if (interior && kt < nfull) {
+            opA.dma(sA, kt * BK, wave);
+            opB.dma(sB, kt * BK, wave);
+        } else {
+            opA.template staged<NT>(sA, kt * BK, tid);
+            opB.template staged<NT>(sB, kt * BK, tid);
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8 fa[FR], fb[FC];
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+                fa[i] = opA.frag(sA, i, kk);
+#pragma unroll
+            for (int j = 0; j < FC; ++j)
+                fb[j] = opB.frag(sB, j, kk);
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int j = 0; j < FC; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
+                                                                        0, 0, 0);
+        }
+        // Every wave's reads of this stage are done before the next overwrite.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    store_tile_lds<FR, FC, WR, WC, BR, BC, EPI>(g, acc, r0, c0, wr, wc, lane, wave, lds,
+                                                lds + 32 * BR * 2);
+}
+
+hipError_t launch_wg2(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
+{
+    TileMap tm;
+    tm.tiles_r = static_cast<int>((p.R + 255) / 256);
+    tm.tiles_c = static_cast<int>((p.C + 127) / 128);
+    tm.group_r = std::min(std::max(group_r, 1), std::max(tm.tiles_r, 1));
+    const int64_t nwg = static_cast<int64_t>(tm.tiles_r) * tm.tiles_c;
+    if (nwg == 0)
+        return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(nwg)), block(256);
+    if (epi == Epi::kAccumF32)
+        hipLaunchKernelGGL((gemm_wg2<2>), grid, block, 0, s, p, tm);
+    else if (epi == Epi::kStoreF32)
+        hipLaunchKernelGGL((gemm_wg2<0>), grid, block, 0, s, p, tm);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <int BR, int BC, int WR, int WC, bool AT, bool BT>
 hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
@@ -1743,6 +1847,18 @@ hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
     const int wgrad_group = LMH_WGRAD_GROUP > 0 ? LMH_WGRAD_GROUP : (p.P <= 256 ? 16 : 8);
     const int64_t tiles256 = ((p.R + 255) / 256) * ((p.C + 255) / 256);
     const int64_t tiles256x128 = ((p.R + 255) / 256) * ((p.C + 127) / 128);
+    // wgrad with at most LMH_WGRAD_WG2 tokens and at least two 256 x 128 tiles
+    // per CU: two workgroups per CU (gemm_wg2).  Measured on MI355X against
+    // gemm_big's 256 x 256 tiles (bit-identical output): M=16 - 256 -8 to -20 %
+    // (M=128 K=4096 V=32768 130.7 -> 116.2 us, K=8192 V=131072 890 -> 711 us),
+    // M=384 -6 %, M=512 -2 %, M=768 +0.5 %, M=1024 +3 %, M=2048 +9 %.
+#ifndef LMH_WGRAD_WG2
+#define LMH_WGRAD_WG2 512
+#endif
+    if constexpr (AT && BT) {
+        if (p.P <= LMH_WGRAD_WG2 && tiles256x128 >= 512)
+            return launch_wg2(p, epi, wgrad_group, s);
+    }
     if (tiles256 >= 256)
         return launch_big<256, 256, 4, 2, AT, BT>(p, epi, BT ? wgrad_group : 8, s);
     if (tiles256x128 >= 192)

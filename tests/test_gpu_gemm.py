@@ -13,7 +13,7 @@ import torch
 import lm_head_fp32_amd as lmh
 import oracle
 import workloads
-from gpu_util import (assert_gemm_close, dev_bf16, host_bits, host_f32, padded_out,
+from gpu_util import (assert_gemm_close, dev_bf16, dev_f32, host_bits, host_f32, padded_out,
                       padding_untouched)
 
 pytestmark = pytest.mark.gpu
@@ -475,3 +475,28 @@ def test_logits_xent_records_benchmark_shape():
     # loss error <= 2 x (max logit error) + FP32 rounding of the statistics
     bound = 2e-5 * S.max(axis=1) + 1e-5 * np.abs(ref[:, 3]) + 1e-6
     assert np.all(np.abs(host_f32(loss)[rows] - ref[:, 3]) <= bound)
+
+
+# wgrad with few tokens and many tiles runs two workgroups per CU (256 x 128
+# tiles, one 64-deep LDS stage).  Integer operands make every dW entry exact,
+# so the check is bit-exact: ragged K (tile rows), ragged V (tile columns),
+# ragged and full token counts, padded leading dimensions, store and
+# accumulate.  Sampled rows of dW include the first and the ragged last ones.
+@pytest.mark.parametrize("M,K,V,pad", [(100, 2056, 8200, 0), (512, 2048, 8192, 8), (1, 2304, 8328, 0),
+                                       (250, 2120, 8208, 16)])
+def test_wgrad_two_per_cu_integer_exact(M, K, V, pad):
+    xb, gb, wb = workloads.integer_operands([(M, K), (M, V), (V, K)], seed=5151 + M)
+    x = dev_bf16(xb, K + pad)
+    g = dev_bf16(gb, V + pad)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(V - 40, V),
+                                     np.random.default_rng(M).integers(0, V, 64)]))
+    dW = lmh.lmhead_wgrad(g, x)
+    torch.cuda.synchronize()
+    ref, _ = oracle.wgrad(gb, xb, rows=rows)
+    assert np.array_equal(host_f32(dW).astype(np.float64)[rows], ref)
+    # accumulate into an existing dW (integer start values): D += tile
+    W0 = oracle.bf16_bits_to_f64(wb).astype(np.float32)
+    acc = dev_f32(W0)
+    lmh.lmhead_wgrad(g, x, dW=acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(acc).astype(np.float64)[rows], ref + W0.astype(np.float64)[rows])
