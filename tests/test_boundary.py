@@ -286,3 +286,15 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         lmh.lmhead_logits(x, x)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and
+    says so, before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stdout
