@@ -39,6 +39,9 @@
  *    written.
  *  - Results are bitwise deterministic run to run; no kernel uses floating
  *    point atomics.
+ *  - No entry point allocates device memory, waits on the stream or the
+ *    device, or enqueues a memset: calls made under stream capture record
+ *    kernel launches only.
  */
 #ifndef LMHEAD_H
 #define LMHEAD_H
