@@ -357,11 +357,16 @@ __global__ __launch_bounds__(WR * WC * 64) void gemm_kernel(GemmProblem g, TileM
 // for any 8 (32-bank) or 16 (64-bank) consecutive lanes.  Global loads for
 // stage k+2 are issued as soon as stage k+1 has been written to LDS and
 // overlap the whole MFMA phase of stage k+1.
+// 256-byte rows (BK = 128, 16 chunks) take a 4-bit key, distinct over any 16
+// consecutive rows.
 template <int BK>
 __device__ __forceinline__ int lds_swz(int row)
 {
-    static_assert(BK == 64, "swizzle defined for 128-byte rows");
-    return (row + (row >> 3)) & 7;
+    static_assert(BK == 64 || BK == 128, "swizzle defined for 128- and 256-byte rows");
+    if constexpr (BK == 64)
+        return (row + (row >> 3)) & 7;
+    else
+        return (row + (row >> 4)) & 15;
 }
 
 __device__ __forceinline__ void lds_barrier()
@@ -1009,11 +1014,11 @@ __device__ __forceinline__ uint16_t *lds_array()
     return buf;
 }
 
-template <int BC, int S, int EPI>
+template <int BC, int S, int EPI, int BK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_small(GemmProblem g, TileMap tm)
 {
-    constexpr int BR = 128, BK = 64, NW = 4;
+    constexpr int BR = 128, NW = 4;
     constexpr int FR = 1, FC = BC / 32;
     using OpA = DmaOperand<BR, BK, NW>;
     using OpB = DmaOperand<BC, BK, NW>;
@@ -1049,10 +1054,10 @@ gemm_small(GemmProblem g, TileMap tm)
     const int fbA = (wave * 32 + lrow) * BK;
     const int fbB = lrow * BK;
     const int keyA = khalf ^ lds_swz<BK>(wave * 32 + lrow);
-    int keyB[2];
+    int keyB[FC];
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-        keyB[par] = khalf ^ lds_swz<BK>(par * 32 + lrow);
+    for (int j = 0; j < FC; ++j)
+        keyB[j] = khalf ^ lds_swz<BK>(j * 32 + lrow);
 
     f32x16 acc[FR][FC];
 #pragma unroll
@@ -1065,16 +1070,15 @@ gemm_small(GemmProblem g, TileMap tm)
         bf16x8 fa[2], fb[2][FC];
         auto fl = [&](int kk, int slot) {
             fa[slot] = *reinterpret_cast<const bf16x8 *>(&lA[fbA + (((2 * kk) ^ keyA) * 8)]);
-            const int kb0 = ((2 * kk) ^ keyB[0]) * 8, kb1 = ((2 * kk) ^ keyB[1]) * 8;
 #pragma unroll
             for (int j = 0; j < FC; ++j)
                 fb[slot][j] = *reinterpret_cast<const bf16x8 *>(
-                    &lB[fbB + j * 32 * BK + ((j & 1) ? kb1 : kb0)]);
+                    &lB[fbB + j * 32 * BK + ((2 * kk) ^ keyB[j]) * 8]);
         };
         fl(0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk + 1 < 4)
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16)
                 fl(kk + 1, (kk + 1) & 1);
 #pragma unroll
             for (int j = 0; j < FC; ++j)
@@ -1144,7 +1148,7 @@ gemm_small(GemmProblem g, TileMap tm)
                                                sA_c(std::integral_constant<int, 0>{}), nullptr);
 }
 
-template <int BC, int S>
+template <int BC, int S, int BK = 64>
 hipError_t launch_small(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
     TileMap tm;
@@ -1155,10 +1159,10 @@ hipError_t launch_small(const GemmProblem &p, Epi epi, int group_r, hipStream_t 
     if (nwg == 0)
         return hipSuccess;
     if (epi == Epi::kStoreBF16)
-        hipLaunchKernelGGL((gemm_small<BC, S, 1>), dim3(static_cast<unsigned>(nwg)), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_small<BC, S, 1, BK>), dim3(static_cast<unsigned>(nwg)), dim3(256), 0,
                            s, p, tm);
     else
-        hipLaunchKernelGGL((gemm_small<BC, S, 0>), dim3(static_cast<unsigned>(nwg)), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_small<BC, S, 0, BK>), dim3(static_cast<unsigned>(nwg)), dim3(256), 0,
                            s, p, tm);
     return hipGetLastError();
 }
@@ -1800,10 +1804,17 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
     if ((LMH_ROWS == 2 ? rows_fits(p) : LMH_ROWS && rows_preferred(p)) &&
         (epi == Epi::kStoreF32 || epi == Epi::kStoreBF16))
         return launch_rows(p, epi, s);
+    // Up to 64 tokens with K <= 4096: 128-deep stages, so each W row is read
+    // in 256-byte runs (rings of 4 and 3 stages fill the 160 KiB of LDS).
+    // Measured on two MI355X against 64-deep stages, V=32768: K=4096 -6 to
+    // -10 % (M=16, 32, 64), M=64 K=1024 -11 to -13 %, other K <= 4096 within
+    // 1 % (M=32 K=1024 +2.5 % on one of the two); at K=8192 0 to +4 %.
     if (p.C <= 32)
-        return launch_small<32, LMH_SMALL_S32>(p, epi, 8, s);
+        return p.P <= 4096 ? launch_small<32, 4, 128>(p, epi, 8, s)
+                           : launch_small<32, LMH_SMALL_S32>(p, epi, 8, s);
     if (p.C <= 64)
-        return launch_small<64, 6>(p, epi, 8, s);
+        return p.P <= 4096 ? launch_small<64, 3, 128>(p, epi, 8, s)
+                           : launch_small<64, 6>(p, epi, 8, s);
     if (p.C <= 256)
         return launch_small<128, LMH_SMALL_S128>(p, epi, 8, s);
     // Many tokens: the ping-pong ring kernel for K <= 8192 (measured 1-3 %
