@@ -203,9 +203,12 @@ static int orc_row_stats(const float *z, int64_t V, int32_t y, int32_t ignore_in
     for (int64_t j = 0; j < V; ++j)
         if ((double)z[j] > m)
             m = (double)z[j];
+    /* A row whose logits are all -inf has no softmax: d is the empty sum 0
+     * (not exp(-inf + inf) = NaN), and the loss below is NaN. */
     double d = 0.0;
-    for (int64_t j = 0; j < V; ++j)
-        d += exp((double)z[j] - m);
+    if (m != -INFINITY)
+        for (int64_t j = 0; j < V; ++j)
+            d += exp((double)z[j] - m);
     *m_out = m;
     *d_out = d;
     if (y == ignore_index) {
@@ -330,9 +333,12 @@ static void orc_xent_partial_rows(void *vctx, int64_t r0, int64_t r1)
             for (int64_t j = j0; j < j1; ++j)
                 if ((double)z[j] > m)
                     m = (double)z[j];
+            /* A block whose logits are all -inf (masked columns) holds no
+             * probability mass: its pair is the empty one, m = -inf, d = 0. */
             double d = 0.0;
-            for (int64_t j = j0; j < j1; ++j)
-                d += exp((double)z[j] - m);
+            if (m != -INFINITY)
+                for (int64_t j = j0; j < j1; ++j)
+                    d += exp((double)z[j] - m);
             double x = 0.0, own = 0.0;
             if (y != c->ignore_index) {
                 int64_t loc = (int64_t)y - c->col0; /* column within the slice */
@@ -382,7 +388,8 @@ void orc_xent_merge(const double *part, int64_t n_parts, int64_t part_stride, in
         int64_t owners = 0;
         for (int64_t p = 0; p < n_parts; ++p) {
             const double *pp = part + p * part_stride + 4 * r;
-            d += pp[1] * exp(pp[0] - m);
+            if (pp[0] != -INFINITY) /* an empty block adds nothing to d */
+                d += pp[1] * exp(pp[0] - m);
             if (pp[3] != 0.0) {
                 x = pp[2];
                 ++owners;

@@ -395,6 +395,60 @@ def test_split_merge_bad_and_unowned_targets():
     assert np.all(np.isfinite(st[:, :2]))
 
 
+def test_masked_columns_carry_no_probability():
+    """Logits of -inf (masked columns) contribute exp(-inf) = 0: a row padded
+    with -inf columns on both sides has the statistics of its finite part
+    (m, X and the sequential d bitwise, since adding 0 is exact), its loss is
+    the unshifted brute-force log-sum-exp over the finite part minus z_y,
+    and its gradient is 0 at every masked column."""
+    rng = np.random.default_rng(17)
+    core = rng.normal(0, 3, (3, 40)).astype(np.float32)
+    t_core = np.array([0, 17, 39], dtype=np.int32)
+    a, b = 4096, 5
+    z = np.full((3, a + 40 + b), -np.inf, dtype=np.float32)
+    z[:, a:a + 40] = core
+    t = t_core + a
+    st = oracle.xent_fwd(z, t, -100)
+    ref = oracle.xent_fwd(core, t_core, -100)
+    assert np.array_equal(st, ref)
+    for i in range(3):
+        lse = _logsumexp_bruteforce(core[i])
+        assert math.isclose(st[i, 3], lse - float(core[i, t_core[i]]), rel_tol=1e-13)
+    g = oracle.xent_bwd(z, t, -100, 0.5)
+    assert np.all(g[:, :a] == 0.0) and np.all(g[:, a + 40:] == 0.0)
+    assert np.array_equal(g[:, a:a + 40], oracle.xent_bwd(core, t_core, -100, 0.5))
+
+
+@pytest.mark.parametrize("bc", [4, 64, 4096])
+def test_split_masked_blocks_are_empty(bc):
+    """A column block whose logits are all -inf reports the empty pair
+    (m_b = -inf, d_b = 0), which the merge skips: the merged statistics of a
+    row whose first 4096 columns are masked equal the full-row forward's."""
+    rng = np.random.default_rng(bc)
+    V = 4096 + 300
+    z = rng.normal(0, 3, (4, V)).astype(np.float32)
+    z[:, :4096] = -np.inf
+    t = np.array([4096, V - 1, 4200, -100], dtype=np.int32)
+    part = oracle.xent_partial(z, t, -100, block_cols=bc)
+    nmasked = 4096 // bc
+    assert np.all(part[:nmasked, :, 0] == -np.inf) and np.all(part[:nmasked, :, 1] == 0.0)
+    st = oracle.xent_merge(part, t, V, -100)
+    ref = oracle.xent_fwd(z, t, -100)
+    assert np.all(np.isfinite(st[:3])) and np.array_equal(st[:, 0], ref[:, 0])
+    assert np.array_equal(st[:, 2], ref[:, 2])
+    np.testing.assert_allclose(st[:, 1], ref[:, 1], rtol=1e-13, atol=0)
+    np.testing.assert_allclose(st[:, 3], ref[:, 3], rtol=1e-12, atol=1e-12)
+
+
+def test_fully_masked_row_has_no_loss():
+    """A row whose logits are all -inf has no softmax: m = -inf, d = 0 (the
+    empty sum) and a NaN loss; an ignored such row still has loss 0."""
+    z = np.full((2, 9), -np.inf, dtype=np.float32)
+    st = oracle.xent_fwd(z, np.array([3, -100], dtype=np.int32), -100)
+    assert np.all(st[:, 0] == -np.inf) and np.all(st[:, 1] == 0.0)
+    assert np.isnan(st[0, 3]) and st[1, 3] == 0.0
+
+
 def test_xent_mean():
     loss = np.array([1.5, 9.0, 2.25, 4.0, 0.5])
     t = np.array([3, -100, 1, -100, 0], np.int32)
