@@ -42,6 +42,14 @@
  *  - No entry point allocates device memory, waits on the stream or the
  *    device, or enqueues a memset: calls made under stream capture record
  *    kernel launches only.
+ *  - Launch limits: one kernel launch holds at most 2^31 work-items.  The
+ *    cross-entropy calls that would need more (e.g. 2^25 rows, or 64-column
+ *    blocks of 8192 x 131072 logits) run as several launches over row ranges,
+ *    with the same results.  A GEMM call whose R x C output (logits: V x M,
+ *    dgrad: K x M, wgrad: K x V) has ceil(R / 128) * ceil(C / 32) > 2^23
+ *    (with a split V sum also 16 ceil(R / 256) ceil(C / 128) > 2^22 or
+ *    C ceil(R / 4) > 2^31) returns LMH_ERR_SHAPE before anything is enqueued;
+ *    such outputs are larger than a GPU's memory.
  */
 #ifndef LMHEAD_H
 #define LMHEAD_H
@@ -151,7 +159,8 @@ int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t
  *          global columns [col0, col0 + n_cols).  Read once.
  *  block_cols  columns per block, a positive multiple of 4; the slice is cut
  *          into n_blocks = ceil(n_cols / block_cols) blocks (the last one may
- *          be shorter).  n_blocks * n_rows must not exceed INT32_MAX.
+ *          be shorter).  n_blocks * n_rows must not exceed INT32_MAX
+ *          (LMH_ERR_SHAPE).
  *  target  int32 [n_rows], GLOBAL column indices; ignore_index as in the
  *          forward.
  *  part    FP32 output, n_blocks arrays of n_rows 16-byte records:
@@ -193,6 +202,11 @@ int32_t lmhead_xent_merge(const float *part, int64_t n_parts, int64_t part_strid
 
 /*
  * lmhead_xent_mean -- mean reduction of the per-row loss
+ *
+ *  Not an operation the pages describe: they state no reduction.  The
+ *  workloads this library is measured on take the mean loss over the rows
+ *  whose target is not ignore_index (-100 there), the usual language-model
+ *  training loss, and its 1 / n_valid is the upstream gradient of every row.
  *
  *  loss     FP32 [n_rows]; target int32 [n_rows] (rows equal to ignore_index
  *           are excluded).  loss may be NULL when mean_out is NULL: 1 / n_valid
@@ -317,6 +331,11 @@ int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t
 
 /*
  * lmhead_wgrad -- weight gradient dW[V x K] (+)= dlogits[M x V]^T . x[M x K]
+ *
+ *  The other GEMM that consumes the BF16 logits gradient ([MIXED] "What does
+ *  this PR do?": the backward casts the gradient to BF16 for the GEMMs that
+ *  follow).  The pages say nothing of dW's type; it is kept in FP32 (the
+ *  GEMM's accumulator), so that it can be accumulated over micro-batches.
  *
  *  dlogits BF16 [M x V], ldd >= V;  x BF16 [M x K], ldx >= K;
  *  dW FP32 [V x K], ldw >= K.  accumulate == 0 overwrites dW; accumulate != 0

@@ -112,6 +112,22 @@ def _dtype_code(dt) -> int:
     return _DT[dt]
 
 
+def _out_code(fn, out, dtype_arg, default):
+    """Element-type code of an output: the passed tensor's own dtype (a
+    conflicting explicit dtype is an error, so that the kernel never stores
+    one type into a buffer of another), else dtype_arg, else the default."""
+    if out is not None:
+        if not isinstance(out, torch.Tensor):
+            raise TypeError(f"{fn}: the output must be a tensor")
+        code = _DT.get(out.dtype)
+        if code is None:
+            raise TypeError(f"{fn}: unsupported output dtype {out.dtype}")
+        if dtype_arg is not None and _dtype_code(dtype_arg) != code:
+            raise ValueError(f"{fn}: the output tensor is {out.dtype}, not {dtype_arg!r}")
+        return code
+    return _dtype_code(default if dtype_arg is None else dtype_arg)
+
+
 def _check(fn, status):
     if status != 0:
         raise LmheadError(fn, status)
@@ -164,10 +180,13 @@ def _empty_rows(rows, cols, dtype, like):
 
 # --------------------------------------------------------------- the calls
 
-def lmhead_logits(x, W, out=None, out_dtype="fp32", stream=None):
+def lmhead_logits(x, W, out=None, out_dtype=None, stream=None):
     """logits[M, V] = x[M, K] . W[V, K]^T; out_dtype 'fp32' keeps the FP32
-    accumulator, 'bf16' rounds it (legacy); 'fp16' is rejected."""
-    code = _dtype_code(out_dtype)
+    accumulator, 'bf16' rounds it (legacy); 'fp16' is rejected.  The default
+    is the output tensor's dtype when `out` is given, else 'bf16': as with
+    the logit-dtype option of Megatron-LM "Add mixed-precision (FP32) LM
+    output logits" (section "Tests"), FP32 logits are opted into."""
+    code = _out_code("lmhead_logits", out, out_dtype, "bf16")
     px, ldx = _mat(x, "x", torch.bfloat16)
     pw, ldw = _mat(W, "W", torch.bfloat16)
     M, K = x.shape
@@ -303,12 +322,13 @@ def lmhead_xent_mean(loss, target, ignore_index=-100, mean=None, inv_nvalid=None
 
 
 def lmhead_xent_bwd(logits, stats, target, dloss, ignore_index=-100, dlogits=None,
-                    grad_dtype="fp32", in_place=False, stream=None):
+                    grad_dtype=None, in_place=False, stream=None):
     """Fused CE backward: dlogits = dloss_i * (softmax - one_hot) in FP32.
 
     dloss: a GPU fp32 tensor of 1 element (every row) or n elements (per row).
-    grad_dtype 'fp32' or 'bf16'; in_place=True writes over `logits` (fp32)."""
-    code = _dtype_code(grad_dtype)
+    grad_dtype 'fp32' or 'bf16' (default: the dtype of `dlogits` when given,
+    else 'fp32'); in_place=True writes over `logits` (fp32)."""
+    code = _out_code("lmhead_xent_bwd", logits if in_place else dlogits, grad_dtype, "fp32")
     pz, ld = _mat(logits, "logits", torch.float32)
     n, V = logits.shape
     ps = _vec(stats, "stats", torch.float32, n * STATS_COLS)
@@ -336,13 +356,13 @@ def lmhead_xent_bwd(logits, stats, target, dloss, ignore_index=-100, dlogits=Non
     return dlogits
 
 
-def lmhead_xent_fused(logits, target, dloss, ignore_index=-100, dlogits=None, grad_dtype="fp32",
+def lmhead_xent_fused(logits, target, dloss, ignore_index=-100, dlogits=None, grad_dtype=None,
                       in_place=False, loss=None, stats=None, stream=None):
     """Forward and backward in one read of the logits, for an upstream
     gradient known before the forward: returns (loss [n], stats [n, 4],
-    dlogits).  dloss as in lmhead_xent_bwd; in_place=True writes the FP32
-    gradient over `logits`."""
-    code = _dtype_code(grad_dtype)
+    dlogits).  dloss and grad_dtype as in lmhead_xent_bwd; in_place=True
+    writes the FP32 gradient over `logits`."""
+    code = _out_code("lmhead_xent_fused", logits if in_place else dlogits, grad_dtype, "fp32")
     pz, ld = _mat(logits, "logits", torch.float32)
     n, V = logits.shape
     pt = _vec(target, "target", torch.int32, n)
@@ -383,7 +403,7 @@ def lmhead_dgrad_workspace_bytes(M, K, V, splits=0):
     return n
 
 
-def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", splits=0, workspace=None, stream=None):
+def lmhead_dgrad(dlogits, W, dX=None, dx_dtype=None, splits=0, workspace=None, stream=None):
     """dX[M, K] = dlogits[M, V] . W[V, K] (bf16 operands, fp32 accumulation).
 
     splits: 0 = the shape's default split of the V sum (lmhead_dgrad_ws; the
@@ -391,8 +411,9 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype="bf16", splits=0, workspace=None,
     lmhead_dgrad_workspace_bytes(M, K, V, splits) bytes, allocated here from
     torch's caching allocator when not given and marked as in use on the
     launch stream; a raw stream handle needs an explicit workspace),
-    1 = the unsplit kernel (lmhead_dgrad), n = n parts."""
-    code = _dtype_code(dx_dtype)
+    1 = the unsplit kernel (lmhead_dgrad), n = n parts.  dx_dtype: the dtype
+    of `dX` when given, else 'bf16' unless stated."""
+    code = _out_code("lmhead_dgrad", dX, dx_dtype, "bf16")
     pd, ldd = _mat(dlogits, "dlogits", torch.bfloat16)
     pw, ldw = _mat(W, "W", torch.bfloat16)
     M, V = dlogits.shape

@@ -20,6 +20,36 @@ constexpr int32_t kMaxSplits = 16;
 // logits GEMM's tile height).
 constexpr int64_t kLogitsStatsBlock = 256;
 
+// Work-items per kernel launch are kept at or below 2^31: the hardware counts
+// a grid dimension's work-items in 32 bits, and the kernels index workgroups
+// with 32-bit integers.  The cross-entropy launchers split longer calls into
+// row ranges themselves; a GEMM call whose grid would pass the limit is
+// refused on the host (LMH_ERR_SHAPE) before anything is enqueued.
+constexpr int64_t kMaxLaunchItems = int64_t{1} << 31;
+
+int64_t ceil_div(int64_t a, int64_t b)
+{
+    return (a + b - 1) / b;
+}
+
+// An upper bound on the work-items of any grid a GEMM with an R x C output
+// can launch.  The densest is the few-token logits kernel, 256 work-items per
+// 128 x 32 tile; the large-tile kernels use at most 512 per 256 x 128 tile.
+// With the contraction split (at most kMaxSplits parts) each part runs
+// 256 x 128 tiles and the reduction one work-item per 4 outputs.
+bool gemm_grid_fits(int64_t R, int64_t C, bool split)
+{
+    const int64_t dense = ceil_div(R, 128) * ceil_div(C, 32);  // <= 2^23 * 2^26
+    if (dense > kMaxLaunchItems / 256)
+        return false;
+    if (split) {
+        const int64_t parts = ceil_div(R, 256) * ceil_div(C, 128) * kMaxSplits;
+        if (parts > kMaxLaunchItems / 512 || C * ceil_div(R, 4) > kMaxLaunchItems)
+            return false;
+    }
+    return true;
+}
+
 bool aligned16(const void *p)
 {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -124,6 +154,8 @@ int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, vo
         if (overlaps(so, span_of(x, M, K, ldx, 2)) || overlaps(so, span_of(W, V, K, ldw, 2)))
             return LMH_ERR_ALIAS;
     }
+    if (!gemm_grid_fits(V, M, false))
+        return LMH_ERR_SHAPE;
     lmh::GemmProblem p;
     p.A = static_cast<const uint16_t *>(W);
     p.lda = ldw;
@@ -167,6 +199,8 @@ int32_t lmhead_logits_xent(const void *x, int64_t ldx, const void *W, int64_t ld
         if (overlaps(so, sx) || overlaps(so, sw) || overlaps(sp, sx) || overlaps(sp, sw))
             return LMH_ERR_ALIAS;
     }
+    if (!gemm_grid_fits(V, M, false))
+        return LMH_ERR_SHAPE;
     lmh::GemmProblem p;
     p.A = static_cast<const uint16_t *>(W);
     p.lda = ldw;
@@ -397,6 +431,8 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
         if (overlaps(so, span_of(dlogits, M, V, ldd, 2)) || overlaps(so, span_of(W, V, K, ldw, 2)))
             return LMH_ERR_ALIAS;
     }
+    if (!gemm_grid_fits(K, M, false))
+        return LMH_ERR_SHAPE;
     lmh::GemmProblem p;
     p.A = static_cast<const uint16_t *>(W);  // stored [V][K] = [P][R]
     p.lda = ldw;
@@ -449,6 +485,8 @@ int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t
     if (overlaps(so, sd) || overlaps(so, sw) || overlaps(ws, so) || overlaps(ws, sd) ||
         overlaps(ws, sw))
         return LMH_ERR_ALIAS;
+    if (!gemm_grid_fits(K, M, true))
+        return LMH_ERR_SHAPE;
     lmh::GemmProblem p;
     p.A = static_cast<const uint16_t *>(W);
     p.lda = ldw;
@@ -482,6 +520,8 @@ int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ld
         if (overlaps(so, span_of(dlogits, M, V, ldd, 2)) || overlaps(so, span_of(x, M, K, ldx, 2)))
             return LMH_ERR_ALIAS;
     }
+    if (!gemm_grid_fits(K, V, false))
+        return LMH_ERR_SHAPE;
     lmh::GemmProblem p;
     p.A = static_cast<const uint16_t *>(x);  // stored [M][K] = [P][R]
     p.lda = ldx;

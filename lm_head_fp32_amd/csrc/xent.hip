@@ -21,6 +21,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace lmh {
 #ifndef LMH_XF_PF
 #define LMH_XF_PF 1
@@ -112,13 +114,17 @@ __device__ __forceinline__ void reduce_row_md(const float *zr, int64_t ncols, in
         for (int u = 1; u < U; ++u)
             bm = fmaxf(bm, max4(v[u]));
         const float mn = fmaxf(m, bm);
-        float acc = d * exp_shifted(m, mn);  // m = -inf gives exp2(-inf) = 0
+        // Shift point: mn, or 0 while every value seen is -inf (masked
+        // columns): then every term below is exp2(-inf) = 0 and the pair
+        // stays empty (m = -inf, d = 0) instead of exp2(-inf + inf) = NaN.
+        const float ms = (mn == -INFINITY) ? 0.0f : mn;
+        float acc = d * exp_shifted(m, ms);  // m = -inf gives exp2(-inf) = 0
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            acc += exp_shifted(v[u].x, mn);
-            acc += exp_shifted(v[u].y, mn);
-            acc += exp_shifted(v[u].z, mn);
-            acc += exp_shifted(v[u].w, mn);
+            acc += exp_shifted(v[u].x, ms);
+            acc += exp_shifted(v[u].y, ms);
+            acc += exp_shifted(v[u].z, ms);
+            acc += exp_shifted(v[u].w, ms);
         }
         d = acc;
         m = mn;
@@ -129,7 +135,8 @@ __device__ __forceinline__ void reduce_row_md(const float *zr, int64_t ncols, in
         if (tid < 4 && j < ncols) {
             const float t = zr[j];
             const float mn = fmaxf(m, t);
-            d = d * exp_shifted(m, mn) + exp_shifted(t, mn);
+            const float ms = (mn == -INFINITY) ? 0.0f : mn;
+            d = d * exp_shifted(m, ms) + exp_shifted(t, ms);
             m = mn;
         }
     }
@@ -557,6 +564,12 @@ __global__ __launch_bounds__(kMeanThreads) void xent_mean_kernel(const float *__
 #define LMH_XB_NTS true
 #endif
 
+// Work-items per launch are kept at or below 2^31 (the hardware counts a
+// grid dimension's work-items in 32 bits): longer calls run as several
+// launches over consecutive row ranges, which changes no result since every
+// workgroup handles whole rows on its own.
+constexpr int64_t kMaxLaunchItems = int64_t{1} << 31;
+
 hipError_t launch_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
                            const int32_t *target, int32_t ignore_index, float *loss, float *stats,
                            hipStream_t s)
@@ -564,16 +577,23 @@ hipError_t launch_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int6
     if (n_rows == 0)
         return hipSuccess;
     float4 *st = reinterpret_cast<float4 *>(stats);
-    if (n_rows < 512) {
-        hipLaunchKernelGGL((xent_fwd_kernel<1024, 4, LMH_XF_NTL>),
-                           dim3(static_cast<unsigned>(n_rows)), dim3(1024), 0, s, logits, ld, n_cols,
-                           target, ignore_index, loss, st);
-    } else {
-        hipLaunchKernelGGL((xent_fwd_kernel<256, LMH_XF_U, LMH_XF_NTL>),
-                           dim3(static_cast<unsigned>(n_rows)), dim3(256), 0, s, logits, ld, n_cols,
-                           target, ignore_index, loss, st);
+    const int nt = n_rows < 512 ? 1024 : 256;
+    const int64_t chunk = kMaxLaunchItems / nt;
+    for (int64_t r0 = 0; r0 < n_rows; r0 += chunk) {
+        const unsigned nr = static_cast<unsigned>(std::min(chunk, n_rows - r0));
+        const float *z = logits + r0 * ld;
+        float *l = loss ? loss + r0 : nullptr;
+        if (nt == 1024)
+            hipLaunchKernelGGL((xent_fwd_kernel<1024, 4, LMH_XF_NTL>), dim3(nr), dim3(1024), 0, s,
+                               z, ld, n_cols, target + r0, ignore_index, l, st + r0);
+        else
+            hipLaunchKernelGGL((xent_fwd_kernel<256, LMH_XF_U, LMH_XF_NTL>), dim3(nr), dim3(256), 0,
+                               s, z, ld, n_cols, target + r0, ignore_index, l, st + r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int64_t n_cols,
@@ -584,24 +604,54 @@ hipError_t launch_xent_partial(const float *logits, int64_t ld, int64_t n_rows, 
     if (n_rows == 0)
         return hipSuccess;
     const int64_t nb = (n_cols + block_cols - 1) / block_cols;
-    hipLaunchKernelGGL((xent_partial_kernel<256, LMH_XF_U, LMH_XF_NTL>),
-                       dim3(static_cast<unsigned>(nb * n_rows)), dim3(256), 0, s, logits, ld,
-                       n_cols, col0, block_cols, nb, target, ignore_index,
-                       reinterpret_cast<float4 *>(part), part_stride / 4);
-    return hipGetLastError();
+    const int64_t max_wg = kMaxLaunchItems / 256;
+    // Launch over [rows r0, r0 + nr) x [blocks b0, b0 + nbc): the slice then
+    // starts at column b0 * block_cols (global column col0 + b0 * block_cols),
+    // so each block keeps its columns and its record slot.
+    auto launch = [&](int64_t r0, int64_t nr, int64_t b0, int64_t nbc) {
+        const int64_t j0 = b0 * block_cols;
+        const int64_t nc = std::min(n_cols - j0, nbc * block_cols);
+        hipLaunchKernelGGL((xent_partial_kernel<256, LMH_XF_U, LMH_XF_NTL>),
+                           dim3(static_cast<unsigned>(nbc * nr)), dim3(256), 0, s,
+                           logits + r0 * ld + j0, ld, nc, col0 + j0, block_cols, nbc, target + r0,
+                           ignore_index, reinterpret_cast<float4 *>(part + b0 * part_stride) + r0,
+                           part_stride / 4);
+        return hipGetLastError();
+    };
+    if (nb <= max_wg) {
+        const int64_t rows_per = max_wg / nb;
+        for (int64_t r0 = 0; r0 < n_rows; r0 += rows_per) {
+            const hipError_t e = launch(r0, std::min(rows_per, n_rows - r0), 0, nb);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int64_t b0 = 0; b0 < nb; b0 += max_wg) {
+            const hipError_t e = launch(r, 1, b0, std::min(max_wg, nb - b0));
+            if (e != hipSuccess)
+                return e;
+        }
+    return hipSuccess;
 }
 
 hipError_t launch_xent_merge(const float *part, int64_t n_parts, int64_t part_stride,
                              int64_t n_rows, const int32_t *target, int32_t ignore_index,
                              int64_t vocab, float *loss, float *stats, hipStream_t s)
 {
-    if (n_rows == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(xent_merge_kernel, dim3(static_cast<unsigned>((n_rows + 3) / 4)),
-                       dim3(256), 0, s, reinterpret_cast<const float4 *>(part), n_parts,
-                       part_stride / 4, n_rows, target, ignore_index, vocab, loss,
-                       reinterpret_cast<float4 *>(stats));
-    return hipGetLastError();
+    const int64_t chunk = kMaxLaunchItems / 64;  // one wavefront per row
+    for (int64_t r0 = 0; r0 < n_rows; r0 += chunk) {
+        const int64_t nr = std::min(chunk, n_rows - r0);
+        hipLaunchKernelGGL(xent_merge_kernel, dim3(static_cast<unsigned>((nr + 3) / 4)), dim3(256),
+                           0, s, reinterpret_cast<const float4 *>(part) + r0, n_parts,
+                           part_stride / 4, nr, target + r0, ignore_index, vocab,
+                           loss ? loss + r0 : nullptr, reinterpret_cast<float4 *>(stats) + r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 // Rows of at most kFusedMaxCols columns fit in the registers of one
@@ -624,24 +674,36 @@ hipError_t launch_xent_fused(const float *logits, int64_t ld, int64_t n_rows, in
         return launch_xent_bwd(logits, ld, stats, target, ignore_index, dloss, dloss_stride,
                                dlogits, ldg, bf16_out, n_rows, n_cols, s);
     }
-    float4 *st = reinterpret_cast<float4 *>(stats);
-    const dim3 grid(static_cast<unsigned>(n_rows)), block(1024);
+    const int64_t chunk = kMaxLaunchItems / 1024;
+    const int64_t gsz = bf16_out ? 2 : 4;
+    for (int64_t r0 = 0; r0 < n_rows; r0 += chunk) {
+        const dim3 grid(static_cast<unsigned>(std::min(chunk, n_rows - r0))), block(1024);
+        const float *z = logits + r0 * ld;
+        const int32_t *t = target + r0;
+        const float *dl = dloss + dloss_stride * r0;
+        float *l = loss ? loss + r0 : nullptr;
+        float4 *st = reinterpret_cast<float4 *>(stats) + r0;
+        void *g = static_cast<char *>(dlogits) + r0 * ldg * gsz;
 #define LMH_FUSED_LAUNCH(PER, BF)                                                               \
-    hipLaunchKernelGGL((xent_fused_kernel<1024, PER, BF>), grid, block, 0, s, logits, ld, n_cols, \
-                       target, ignore_index, dloss, dloss_stride, loss, st, dlogits, ldg)
-    if (n_cols <= 4 * 1024 * 8) {
-        if (bf16_out)
-            LMH_FUSED_LAUNCH(8, true);
-        else
-            LMH_FUSED_LAUNCH(8, false);
-    } else {
-        if (bf16_out)
-            LMH_FUSED_LAUNCH(16, true);
-        else
-            LMH_FUSED_LAUNCH(16, false);
-    }
+    hipLaunchKernelGGL((xent_fused_kernel<1024, PER, BF>), grid, block, 0, s, z, ld, n_cols, t,   \
+                       ignore_index, dl, dloss_stride, l, st, g, ldg)
+        if (n_cols <= 4 * 1024 * 8) {
+            if (bf16_out)
+                LMH_FUSED_LAUNCH(8, true);
+            else
+                LMH_FUSED_LAUNCH(8, false);
+        } else {
+            if (bf16_out)
+                LMH_FUSED_LAUNCH(16, true);
+            else
+                LMH_FUSED_LAUNCH(16, false);
+        }
 #undef LMH_FUSED_LAUNCH
-    return hipGetLastError();
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_xent_mean(const float *loss, const int32_t *target, int32_t ignore_index,
@@ -664,17 +726,27 @@ hipError_t launch_xent_bwd(const float *logits, int64_t ld, const float *stats,
     int64_t bpr = (n4 + NT * U - 1) / (NT * U);
     if (bpr < 1)
         bpr = 1;  // rows shorter than 4 columns still need the tail block
-    const int64_t nblk = bpr * n_rows;
+    const int64_t chunk = std::max<int64_t>(1, kMaxLaunchItems / NT / bpr);
+    const int64_t gsz = bf16_out ? 2 : 4;
     const float4 *st = reinterpret_cast<const float4 *>(stats);
-    if (bf16_out)
-        hipLaunchKernelGGL((xent_bwd_kernel<NT, U, true, LMH_XB_NTL, LMH_XB_NTS>),
-                           dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s, logits, ld, st, target,
-                           ignore_index, dloss, dloss_stride, dlogits, ldg, n_cols, bpr);
-    else
-        hipLaunchKernelGGL((xent_bwd_kernel<NT, U, false, LMH_XB_NTL, LMH_XB_NTS>),
-                           dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, s, logits, ld, st, target,
-                           ignore_index, dloss, dloss_stride, dlogits, ldg, n_cols, bpr);
-    return hipGetLastError();
+    for (int64_t r0 = 0; r0 < n_rows; r0 += chunk) {
+        const unsigned nblk = static_cast<unsigned>(bpr * std::min(chunk, n_rows - r0));
+        const float *z = logits + r0 * ld;
+        const float *dl = dloss + dloss_stride * r0;
+        void *g = static_cast<char *>(dlogits) + r0 * ldg * gsz;
+        if (bf16_out)
+            hipLaunchKernelGGL((xent_bwd_kernel<NT, U, true, LMH_XB_NTL, LMH_XB_NTS>), dim3(nblk),
+                               dim3(NT), 0, s, z, ld, st + r0, target + r0, ignore_index, dl,
+                               dloss_stride, g, ldg, n_cols, bpr);
+        else
+            hipLaunchKernelGGL((xent_bwd_kernel<NT, U, false, LMH_XB_NTL, LMH_XB_NTS>), dim3(nblk),
+                               dim3(NT), 0, s, z, ld, st + r0, target + r0, ignore_index, dl,
+                               dloss_stride, g, ldg, n_cols, bpr);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace lmh

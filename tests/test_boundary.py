@@ -267,6 +267,33 @@ def test_dgrad_workspace_and_split_validation(L):
     assert f(A, 120, B, 64, C, 64, BF16, 16, 64, 128, 0, None, 0, None) == SHAPE  # ldd < V
 
 
+def test_gemm_grid_limits(L):
+    """A GEMM whose grid would pass 2^31 work-items is refused on the host
+    (LMH_ERR_SHAPE) before anything is enqueued.  The densest grid is the
+    few-token kernel's, 256 work-items per 128 x 32 output tile, so the bound
+    is ceil(R / 128) * ceil(C / 32) <= 2^23 for an R x C output; with the V sum
+    split the parts' 256 x 128 tiles (16 parts at most) and the reduction's
+    one work-item per 4 outputs bound it as well.  Operands sit at fake
+    addresses far apart, so only the grid check can fail."""
+    X, Y, Z, WS = 1 << 40, 1 << 42, 1 << 50, 1 << 56
+    # logits M = 2^20 tokens x V = 2^22: ceil(V/128) * ceil(M/32) = 2^32 tiles
+    assert L.lmhead_logits(X, 8, Y, 8, Z, 1 << 22, FP32, 1 << 20, 8, 1 << 22, None) == SHAPE
+    assert L.lmhead_logits_xent(X, 8, Y, 8, Z, 1 << 22, 1 << 20, 8, 1 << 22, WS, -100,
+                                WS + (1 << 30), 4 << 20, None) == SHAPE
+    # wgrad dW [2^22 x 2^16]: R = K = 2^16, C = V = 2^22 -> 2^9 * 2^17 tiles
+    assert L.lmhead_wgrad(X, 1 << 22, Y, 1 << 16, Z, 1 << 16, 0, 8, 1 << 16, 1 << 22,
+                          None) == SHAPE
+    # dgrad dX [2^20 x 2^16]: R = K = 2^16, C = M = 2^20 -> 2^9 * 2^15 tiles
+    assert L.lmhead_dgrad(X, 8, Y, 1 << 16, Z, 1 << 16, FP32, 1 << 20, 1 << 16, 8,
+                          None) == SHAPE
+    # split dgrad M = K = 2^17 (dX 2^34 outputs): the unsplit grid would fit
+    # (2^10 * 2^12 dense tiles) but 16 parts of 256 x 128 tiles do not
+    need = L.lmhead_dgrad_workspace_bytes(1 << 17, 1 << 17, 1 << 13, 2)
+    assert need == 2 * (1 << 34) * 4
+    assert L.lmhead_dgrad_ws(X, 1 << 13, Y, 1 << 17, Z, 1 << 17, FP32, 1 << 17, 1 << 17,
+                             1 << 13, 2, WS, need, None) == SHAPE
+
+
 def test_diag_mfma_loop_validation(L):
     f = L.lmhead_diag_mfma_loop
     for mode in (0, 1):
@@ -286,6 +313,34 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         lmh.lmhead_logits(x, x)
+
+
+def test_binding_output_dtype_follows_the_tensor():
+    """The binding never stores one element type into a buffer of another: a
+    passed output tensor sets the type, and a conflicting explicit dtype is an
+    error raised before any pointer is read.  The logits default to BF16 when
+    no output is passed (FP32 logits are opted into, as with the pages' logit
+    dtype option)."""
+    import inspect
+    import torch
+    z = torch.zeros(4, 8, dtype=torch.float32)
+    t = torch.zeros(4, dtype=torch.int32)
+    gb = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lmh.lmhead_xent_bwd(z, z, t, z, dlogits=gb, grad_dtype="fp32")
+    with pytest.raises(ValueError):
+        lmh.lmhead_xent_fused(z, t, z, dlogits=gb, grad_dtype="fp32")
+    with pytest.raises(ValueError):
+        lmh.lmhead_xent_bwd(z, z, t, z, in_place=True, grad_dtype="bf16")
+    with pytest.raises(ValueError):
+        lmh.lmhead_logits(gb, gb, out=z, out_dtype="bf16")
+    with pytest.raises(ValueError):
+        lmh.lmhead_dgrad(gb, gb, dX=z, dx_dtype="bf16")
+    assert lmh._out_code("f", None, None, "bf16") == lmh.LMH_BF16
+    assert lmh._out_code("f", z, None, "bf16") == lmh.LMH_FP32
+    assert lmh._out_code("f", gb, "bf16", "fp32") == lmh.LMH_BF16
+    assert inspect.signature(lmh.lmhead_logits).parameters["out_dtype"].default is None
+    assert "'bf16'" in lmh.lmhead_logits.__doc__
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -313,12 +313,151 @@ def test_xent_131k_spikes_inplace():
     assert np.all(np.abs(ss[:, 1] - sh[:, 1]) <= 1e-5 * sh[:, 1])
     _check_stats(ss[rows], st_ref, "131k split")
     del part, loss_s, st_s
+    # 64-column blocks: 2048 x 8192 = 2^24 workgroups, more than one launch
+    # may hold (2^32 work-items), so the library splits the call into row
+    # ranges; the merged statistics are those of the one-pass forward
+    part = lmh.lmhead_xent_partial(z, t, block_cols=64)
+    loss_s, st_s = lmh.lmhead_xent_merge(part, t, V)
+    torch.cuda.synchronize()
+    ss = host_f32(st_s)
+    assert np.array_equal(_bits(ss[:, 0]), _bits(sh[:, 0]))
+    assert np.array_equal(_bits(ss[:, 2]), _bits(sh[:, 2]))
+    assert np.all(np.abs(ss[:, 1] - sh[:, 1]) <= 1e-5 * sh[:, 1])
+    del part, loss_s, st_s
     # in place over the logits (the copy keeps z for nothing else)
     g = lmh.lmhead_xent_bwd(z, st, t, inv)
     zc = z.clone()
     lmh.lmhead_xent_bwd(zc, st, t, inv, in_place=True)
     torch.cuda.synchronize()
     assert torch.equal(zc.view(torch.int32), g.view(torch.int32))
+    del zc
+    # The same backward with unit upstream gradient: its largest entries are
+    # near 1 (p_y - 1), so the 1e-6 absolute bar is a tight relative check
+    # (with dloss = 1/8028 above it allowed ~1 % of the largest gradient).
+    one = torch.ones((1,), dtype=torch.float32, device="cuda")
+    g1 = lmh.lmhead_xent_bwd(z, st, t, one, dlogits=g)
+    torch.cuda.synchronize()
+    g1_ref = oracle.xent_bwd(inp.logits, inp.target, -100, 1.0, rows=rows)
+    gh1 = host_f32(g1[torch.from_numpy(rows).cuda()])
+    assert np.abs(g1_ref).max() > 0.5
+    _check_grad(gh1, g1_ref, 1e-6, "dlogits, dloss = 1")
+
+
+# ---------------------------------------------------- masked (-inf) logits
+
+def _masked_logits(n, V, seed):
+    """Rows with -inf (masked) columns: leading 4096 columns masked, all but
+    the 3 tail columns masked, trailing columns masked, none masked."""
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0.0, 3.0, (n, V)).astype(np.float32)
+    t = np.empty(n, dtype=np.int32)
+    for i in range(n):
+        kind = i % 4
+        if kind == 0:
+            z[i, :4096] = -np.inf
+            t[i] = rng.integers(4096, V)
+        elif kind == 1:
+            z[i, :V - 3] = -np.inf
+            t[i] = V - 1 - (i % 3)
+        elif kind == 2:
+            z[i, 5000:] = -np.inf
+            t[i] = rng.integers(0, 5000)
+        else:
+            t[i] = rng.integers(0, V)
+    t[5::7] = -100
+    return z, t
+
+
+@pytest.mark.parametrize("n", [9, 520])
+def test_masked_columns_forward_split_fused_backward(n):
+    """Logits of -inf contribute nothing (exp(-inf) = 0): whole 4-value groups,
+    whole column blocks and rows masked up to their ragged tail.  The one-pass
+    forward (1024- and 256-thread forms), the split forward in 64- and
+    4096-column blocks (masked blocks report the empty pair m = -inf, d = 0),
+    the fused single-read kernel and the backward all match the oracle, with
+    exact zeros at the masked columns."""
+    V = 4096 + 3000 + 3
+    z_h, t_h = _masked_logits(n, V, seed=n)
+    _say(f"masked logits n={n} V={V}")
+    z, t = dev_f32(z_h), dev_i32(t_h)
+    loss, st = lmh.lmhead_xent_fwd(z, t)
+    dl = torch.full((1,), 0.5, device="cuda")
+    g = lmh.lmhead_xent_bwd(z, st, t, dl)
+    lf, sf, gf = lmh.lmhead_xent_fused(z, t, dl)
+    parts = {bc: lmh.lmhead_xent_partial(z, t, block_cols=bc) for bc in (64, 4096)}
+    merged = {bc: lmh.lmhead_xent_merge(p, t, V)[1] for bc, p in parts.items()}
+    torch.cuda.synchronize()
+    ref = oracle.xent_fwd(z_h, t_h, -100)
+    assert np.isfinite(ref).all()
+    _check_stats(host_f32(st), ref, "fwd")
+    _check_stats(host_f32(sf), ref, "fused")
+    for bc in parts:
+        _check_part(host_f32(parts[bc]), oracle.xent_partial(z_h, t_h, block_cols=bc),
+                    f"part {bc}")
+        _check_stats(host_f32(merged[bc]), ref, f"merge {bc}")
+    g_ref = oracle.xent_bwd(z_h, t_h, -100, 0.5)
+    _check_grad(host_f32(g), g_ref, 1e-6, "bwd")
+    _check_grad(host_f32(gf), g_ref, 1e-6, "fused")
+    masked = np.isneginf(z_h)
+    assert np.all(host_f32(g)[masked] == 0.0) and np.all(host_f32(gf)[masked] == 0.0)
+
+
+def test_fully_masked_row():
+    """A row of -inf logits has no softmax: m = -inf, d = 0 and a NaN loss, as
+    in the oracle; an ignored such row has loss 0; other rows are unaffected."""
+    z_h = np.random.default_rng(3).normal(0, 1, (3, 40)).astype(np.float32)
+    z_h[0] = -np.inf
+    z_h[1] = -np.inf
+    t_h = np.array([7, -100, 7], dtype=np.int32)
+    loss, st = lmh.lmhead_xent_fwd(dev_f32(z_h), dev_i32(t_h))
+    torch.cuda.synchronize()
+    sh, ref = host_f32(st), oracle.xent_fwd(z_h, t_h, -100)
+    assert np.all(sh[:2, 0] == -np.inf) and np.all(sh[:2, 1] == 0.0)
+    assert np.isnan(sh[0, 3]) and np.isnan(ref[0, 3])
+    assert sh[1, 3] == 0.0 and ref[1, 3] == 0.0
+    _check_stats(sh[2:], ref[2:], "unmasked row")
+
+
+# ------------------------------------ calls longer than one launch can hold
+
+def test_many_rows_split_into_several_launches():
+    """2^25 + 3 rows of 4 columns: the forward (256 work-items per row), the
+    backward (128 per row), the fused kernel (1024 per row), the split forward
+    and the merge all need more than 2^31 work-items, so the library runs each
+    as several launches over row ranges.  Rows on both sides of every range
+    boundary, and others, match the oracle; nothing is left unwritten."""
+    n, V = (1 << 25) + 3, 4
+    rng = np.random.default_rng(workloads.SEED + 25)
+    z_h = rng.standard_normal((n, V), dtype=np.float32) * np.float32(3.0)
+    t_h = rng.integers(0, V, n).astype(np.int32)
+    t_h[rng.choice(n, n // 50, replace=False)] = -100
+    _say(f"many rows n={n} V={V}")
+    z, t = dev_f32(z_h), dev_i32(t_h)
+    dl = torch.full((1,), 0.25, device="cuda")
+    loss, st = lmh.lmhead_xent_fwd(z, t)
+    g = lmh.lmhead_xent_bwd(z, st, t, dl)
+    lf, sf, gf = lmh.lmhead_xent_fused(z, t, dl)
+    part = lmh.lmhead_xent_partial(z, t, block_cols=4)
+    lm, sm = lmh.lmhead_xent_merge(part, t, V)
+    _, inv = lmh.lmhead_xent_mean(None, t)
+    torch.cuda.synchronize()
+    for name, a in (("fwd", st), ("fused", sf), ("merge", sm)):
+        assert torch.isfinite(a[:, :2]).all().item(), name
+        assert torch.isfinite(a[:, 3]).all().item(), name
+    assert torch.isfinite(g).all().item() and torch.isfinite(gf).all().item()
+    edges = np.arange(1, 17) << 21
+    rows = np.unique(np.concatenate([(edges[:, None] + np.arange(-2, 2)[None, :]).ravel(),
+                                     rng.integers(0, n, 300), [0, n - 1]]))
+    rows = rows[(rows >= 0) & (rows < n)]
+    rt = torch.from_numpy(rows).cuda()
+    ref = oracle.xent_fwd(z_h, t_h, -100, rows=rows)
+    for name, a in (("fwd", st), ("fused", sf), ("merge", sm)):
+        _check_stats(host_f32(a[rt]), ref, name)
+    g_ref = oracle.xent_bwd(z_h, t_h, -100, 0.25, rows=rows)
+    _check_grad(host_f32(g[rt]), g_ref, 1e-6, "bwd")
+    _check_grad(host_f32(gf[rt]), g_ref, 1e-6, "fused")
+    nv = int((t_h != -100).sum())
+    assert float(host_f32(inv)[0]) == np.float32(1.0 / nv)
 
 
 # ------------------------------------------------ split-vocabulary forward
