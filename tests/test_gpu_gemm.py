@@ -55,14 +55,19 @@ def test_logits_tiny_exact_fp32_and_bf16():
 @pytest.mark.parametrize("K", workloads.INT_SWEEP_K)
 def test_logits_integer_sweep_v32768(K):
     """The pages' integer sweep: 16 x K activations, 32,768 x K weights,
-    K = 512 ... 16384; FP32 logits bit-exact (rows sampled for the oracle)."""
+    K = 512 ... 16384; every raw FP32 output word equals the oracle's exact
+    value (no tolerance), and every BF16 output word is its nearest-even
+    rounding."""
     inp = workloads.integer_gemm(16, K, 32768, seed=workloads.SEED, with_targets=False)
     _say(f"int sweep K={K}")
-    out = lmh.lmhead_logits(dev_bf16(inp.x), dev_bf16(inp.W), out_dtype="fp32")
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    out = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    outb = lmh.lmhead_logits(x, W, out_dtype="bf16")
     torch.cuda.synchronize()
-    rows = np.array([0, 7, 15])
-    L, _ = oracle.logits(inp.x, inp.W, rows=rows)
-    assert np.array_equal(_f32_bits(host_f32(out)[rows]), _f32_bits(L.astype(np.float32)))
+    L, _ = oracle.logits(inp.x, inp.W, with_abs=False)
+    assert L.shape == (16, 32768)
+    assert np.array_equal(_f32_bits(host_f32(out)), _f32_bits(L.astype(np.float32)))
+    assert np.array_equal(host_bits(outb), oracle.round_bf16(L))
 
 
 def _up(v, m):
@@ -77,6 +82,10 @@ def _up(v, m):
     (260, 32, 300, 0), (300, 64, 260, 8), (270, 224, 513, 0), (512, 256, 520, 8),
     # many tokens on the 64-wide-stage kernel: K not a multiple of 32, K > 8192
     (300, 200, 700, 8), (264, 8224, 300, 0),
+    # up to 64 tokens with K <= 4096: 128-deep stages (rings of 4 and 3), the
+    # steady loop from 5 full stages on, ragged 128-deep tails (K = 1000)
+    (40, 1024, 1000, 8), (64, 1000, 4100, 0), (64, 4096, 2049, 8), (40, 4096, 300, 16),
+    (33, 1000, 777, 0), (16, 4096, 3000, 8), (64, 1024, 33, 0),
 ])
 def test_logits_ragged_integer_exact(M, K, V, pad):
     """Ragged M, K, V (partial tiles on every edge, K not a multiple of the
@@ -159,7 +168,7 @@ def test_logits_lmhead_128_random_full():
 
 
 def test_logits_lmhead_1024_random_sampled():
-    """M=1024, K=8192, V=32768 (the benchmark's launch shape): 24 sampled
+    """M=1024, K=8192, V=32768 (the benchmark's launch shape): 64 sampled
     rows x all V columns within 1e-5 * S; run twice, bitwise identical; the
     BF16 output is the nearest-even rounding of the FP32 one everywhere."""
     inp = workloads.lmhead_1024()
@@ -171,7 +180,9 @@ def test_logits_lmhead_1024_random_sampled():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
     assert torch.equal(outb.cpu().view(torch.int16), out.cpu().to(torch.bfloat16).view(torch.int16))
-    rows = np.concatenate([np.arange(0, 1024, 64), [1, 255, 256, 511, 512, 767, 1022, 1023]])
+    rows = np.unique(np.concatenate([np.arange(0, 1024, 32), [1, 255, 256, 511, 512, 767, 1022, 1023],
+                                     np.random.default_rng(64).integers(0, 1024, 40)]))[:64]
+    assert rows.size == 64
     L, S = oracle.logits(inp.x, inp.W, rows=rows)
     assert_gemm_close(host_f32(out)[rows], L, S, 1e-5, "fp32 logits 1024")
 
@@ -327,11 +338,10 @@ def test_wgrad_integer_exact_and_accumulate(M, K, V):
 
 
 def test_wgrad_pipelined_integer_exact():
-    """wgrad with enough tiles for the pipelined persistent kernel (each tile's
-    FP32 results stored during the next tile's stages), ragged in K and V
-    (edge tiles both ways), into a NaN-filled padded dW: no element left
-    unwritten, padding untouched, and bit-exact rows at both V edges and in
-    between against the oracle."""
+    """wgrad at 96 tokens with many tiles (the two-workgroups-per-CU kernel),
+    ragged in K and V (edge tiles both ways), into a NaN-filled padded dW: no
+    element left unwritten, padding untouched, and bit-exact rows at both V
+    edges and in between against the oracle."""
     M, K, V = 96, 4100, 16500
     dl_bits, x_bits = workloads.integer_operands([(M, V), (M, K)], seed=77)
     _say(f"wgrad pipelined int M={M} K={K} V={V}")
@@ -377,8 +387,9 @@ def test_logits_integer_exact_interior_tiles():
 
 
 def test_dgrad_integer_exact_interior_tiles():
-    """M=1024 K=8192 V=4096: dgrad runs 256x128 8-wave tiles with the
-    register-transposed W operand; sampled rows bit-exact."""
+    """M=1024 K=8192 V=4096: dgrad with its default V split in two (256x256
+    8-wave tiles, FP32 partials reduced in order), the p-major W operand read
+    through transposing LDS loads; sampled rows bit-exact."""
     dl_bits, W_bits = workloads.integer_operands([(1024, 4096), (4096, 8192)], seed=41)
     _say("dgrad int interior 1024x8192x4096")
     dX = lmh.lmhead_dgrad(dev_bf16(dl_bits), dev_bf16(W_bits), dx_dtype="fp32")
@@ -389,8 +400,9 @@ def test_dgrad_integer_exact_interior_tiles():
 
 
 def test_wgrad_integer_exact_interior_tiles():
-    """M=2048 K=4096 V=8192: wgrad runs 256x256 4-wave tiles with both
-    operands register-transposed; sampled rows bit-exact, then accumulate."""
+    """M=2048 K=4096 V=8192: wgrad runs 256x256 8-wave tiles with both
+    p-major operands read through transposing LDS loads; sampled rows
+    bit-exact, then accumulate."""
     dl_bits, x_bits = workloads.integer_operands([(2048, 8192), (2048, 4096)], seed=43)
     _say("wgrad int interior 2048x4096x8192")
     dl, x = dev_bf16(dl_bits), dev_bf16(x_bits)
