@@ -36,7 +36,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# $LMH_ORACLE_LIB selects another build of oracle.c (the sanitized one).
+_LIB_PATH = os.environ.get("LMH_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _i64 = ctypes.c_int64
@@ -51,7 +52,7 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         from . import build as _build
 
-        _build.build()
+        _build.build(sanitize=_LIB_PATH == _build.SAN_LIB)
     lib = ctypes.CDLL(_LIB_PATH)
     lib.orc_gemm_bf16.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64,
                                   _i64, _vp, _i64, _i64, _vp, _vp, ctypes.c_int]
