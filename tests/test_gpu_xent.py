@@ -379,7 +379,7 @@ def test_masked_columns_forward_split_fused_backward(n):
     V = 4096 + 3000 + 3
     z_h, t_h = _masked_logits(n, V, seed=n)
     _say(f"masked logits n={n} V={V}")
-    z, t = dev_f32(z_h), dev_i32(t_h)
+    z, t = dev_f32(z_h, V + 1), dev_i32(t_h)        # rows padded to a multiple of 4
     loss, st = lmh.lmhead_xent_fwd(z, t)
     dl = torch.full((1,), 0.5, device="cuda")
     g = lmh.lmhead_xent_bwd(z, st, t, dl)
