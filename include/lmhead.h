@@ -71,7 +71,8 @@ enum lmh_status {
     LMH_ERR_NULL = 3,   /* required pointer is NULL                          */
     LMH_ERR_ALIGN = 4,  /* pointer not 16-B aligned or ld not a multiple     */
     LMH_ERR_ALIAS = 5,  /* an output overlaps an input in an unsupported way */
-    LMH_ERR_LAUNCH = 6  /* the HIP launch failed (see hipGetLastError)       */
+    LMH_ERR_LAUNCH = 6, /* the HIP launch failed (see hipGetLastError)       */
+    LMH_ERR_SCRATCH = 7 /* needs more than the fixed scratch array holds     */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -328,6 +329,30 @@ int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t
                         void *dX, int64_t ldx, int32_t dx_dtype,
                         int64_t M, int64_t K, int64_t V, int32_t splits,
                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * lmhead_dgrad_noalloc -- lmhead_dgrad_ws with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ *  Same arguments, split choice, kernels and results as lmhead_dgrad_ws
+ *  (bitwise, for the same splits); the FP32 partial sums go to a fixed device
+ *  array of LMH_DGRAD_NOALLOC_MAX_BYTES (64 MiB) that the library holds on
+ *  each GPU it runs on until the process ends.  Shapes whose split needs more
+ *  than that (lmhead_dgrad_workspace_bytes(M, K, V, splits) >
+ *  LMH_DGRAD_NOALLOC_MAX_BYTES) return LMH_ERR_SCRATCH before anything is
+ *  enqueued; shapes that run unsplit are lmhead_dgrad.  The first call on a
+ *  device looks up the array's device address (with that device current); the
+ *  call never allocates, frees or clears memory.  Every call on one GPU
+ *  shares that GPU's array: calls that may overlap on one GPU (different
+ *  streams, or host threads without ordering) race and must be serialised
+ *  by the caller.  Nothing needs the array zeroed: every partial is written
+ *  before it is read.
+ */
+#define LMH_DGRAD_NOALLOC_MAX_BYTES (((int64_t)64) << 20)
+int32_t lmhead_dgrad_noalloc(const void *dlogits, int64_t ldd, const void *W, int64_t ldw,
+                             void *dX, int64_t ldx, int32_t dx_dtype,
+                             int64_t M, int64_t K, int64_t V, int32_t splits, void *stream);
 
 /*
  * lmhead_wgrad -- weight gradient dW[V x K] (+)= dlogits[M x V]^T . x[M x K]

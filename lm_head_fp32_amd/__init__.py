@@ -57,7 +57,11 @@ _SIGNATURES = {
     "lmhead_dgrad_workspace_bytes": ([_i64, _i64, _i64, _i32], _i64),
     "lmhead_dgrad_ws": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
                          _vp], _i32),
+    "lmhead_dgrad_noalloc": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _i32,
+                              _vp], _i32),
 }
+
+DGRAD_NOALLOC_MAX_BYTES = 64 << 20  # LMH_DGRAD_NOALLOC_MAX_BYTES in lmhead.h
 
 
 class LmheadError(RuntimeError):
@@ -447,6 +451,27 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype=None, splits=0, workspace=None, s
     _check("lmhead_dgrad_ws", lib().lmhead_dgrad_ws(pd, ldd, pw, ldw, px, ldx, code, M, K, V, splits,
                                                     workspace.data_ptr(), nbytes,
                                                     _stream(stream)))
+    return dX
+
+
+def lmhead_dgrad_noalloc(dlogits, W, dX, dx_dtype=None, splits=0, stream=None):
+    """lmhead_dgrad with the V-split partial sums in the library's fixed
+    per-GPU scratch array (at most DGRAD_NOALLOC_MAX_BYTES) instead of a
+    workspace: neither this call nor the library allocates.  dX must be
+    passed.  Calls that may overlap on one GPU race on that array."""
+    code = _out_code("lmhead_dgrad_noalloc", dX, dx_dtype, "bf16")
+    pd, ldd = _mat(dlogits, "dlogits", torch.bfloat16)
+    pw, ldw = _mat(W, "W", torch.bfloat16)
+    M, V = dlogits.shape
+    K = W.shape[1]
+    if W.shape[0] != V:
+        raise ValueError("dlogits and W disagree on V")
+    px, ldx = _mat(dX, "dX", dX.dtype)
+    if dX.shape != (M, K):
+        raise ValueError("dX must be [M, K]")
+    _check("lmhead_dgrad_noalloc",
+           lib().lmhead_dgrad_noalloc(pd, ldd, pw, ldw, px, ldx, code, M, K, V, int(splits),
+                                      _stream(stream)))
     return dX
 
 

@@ -10,6 +10,17 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+// The fixed scratch array of lmhead_dgrad_noalloc: the V-split dgrad's FP32
+// partial sums live here instead of in a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side handle, not device memory: kernels and copies
+// take the device address that hipGetSymbolAddress returns for the current
+// device (scratch_device_address below), never the name itself.
+static __device__ __align__(256) float scratch[LMH_DGRAD_NOALLOC_MAX_BYTES / 4];
+
 namespace {
 
 constexpr int64_t kMaxDim = static_cast<int64_t>(INT_MAX);
@@ -113,6 +124,71 @@ int32_t check_dtype_out(int32_t dt)
     return (dt == LMH_BF16 || dt == LMH_FP32) ? LMH_OK : LMH_ERR_DTYPE;
 }
 
+// --------------------------------------------------------------------------
+// The per-device address of the fixed scratch array (defined at file scope
+// above the namespace), looked up once per device.
+constexpr int64_t kScratchBytes = LMH_DGRAD_NOALLOC_MAX_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made on that device (with it current) and kept for later calls.
+int32_t scratch_device_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return LMH_ERR_LAUNCH;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return LMH_ERR_LAUNCH;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LMH_OK;
+}
+
+// Checks shared by the two split-dgrad entry points: operands, outputs and
+// their overlaps, and the grid limit (everything but the workspace).
+int32_t check_dgrad_split(const void *dlogits, int64_t ldd, const void *W, int64_t ldw,
+                          void *dX, int64_t ldx, int32_t dx_dtype, int64_t M, int64_t K,
+                          int64_t V)
+{
+    const int64_t osz = dx_dtype == LMH_FP32 ? 4 : 2;
+    LMH_TRY(check_matrix(dX, M, K, ldx, dx_dtype == LMH_FP32 ? 4 : 8));
+    LMH_TRY(check_matrix(dlogits, M, V, ldd, 8));
+    LMH_TRY(check_matrix(W, V, K, ldw, 8));
+    const Span so = span_of(dX, M, K, ldx, osz);
+    if (overlaps(so, span_of(dlogits, M, V, ldd, 2)) || overlaps(so, span_of(W, V, K, ldw, 2)))
+        return LMH_ERR_ALIAS;
+    if (!gemm_grid_fits(K, M, true))
+        return LMH_ERR_SHAPE;
+    return LMH_OK;
+}
+
+int32_t launch_dgrad_split(const void *dlogits, int64_t ldd, const void *W, int64_t ldw,
+                           void *dX, int64_t ldx, int32_t dx_dtype, int64_t M, int64_t K,
+                           int64_t V, int32_t splits, float *ws, void *stream)
+{
+    lmh::GemmProblem p;
+    p.A = static_cast<const uint16_t *>(W);
+    p.lda = ldw;
+    p.B = static_cast<const uint16_t *>(dlogits);
+    p.ldb = ldd;
+    p.D = dX;
+    p.ldd = ldx;
+    p.R = K;
+    p.C = M;
+    p.P = V;
+    return launch_status(lmh::launch_gemm_dgrad_split(p, dx_dtype != LMH_FP32, splits, ws,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,13 +203,15 @@ const char *lmhead_status_str(int32_t status)
     case LMH_ERR_ALIGN: return "LMH_ERR_ALIGN: pointer or leading dimension misaligned";
     case LMH_ERR_ALIAS: return "LMH_ERR_ALIAS: output overlaps an input";
     case LMH_ERR_LAUNCH: return "LMH_ERR_LAUNCH: kernel launch failed";
+    case LMH_ERR_SCRATCH:
+        return "LMH_ERR_SCRATCH: needs more scratch than the library's fixed array holds";
     default: return "unknown lmhead status";
     }
 }
 
 int32_t lmhead_version(void)
 {
-    return 103;
+    return 104;
 }
 
 int32_t lmhead_logits(const void *x, int64_t ldx, const void *W, int64_t ldw, void *out,
@@ -467,7 +545,6 @@ int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t
     const int64_t need = 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
     if (need == 0)
         return lmhead_dgrad(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V, stream);
-    const int64_t osz = dx_dtype == LMH_FP32 ? 4 : 2;
     LMH_TRY(check_matrix(dX, M, K, ldx, dx_dtype == LMH_FP32 ? 4 : 8));
     LMH_TRY(check_matrix(dlogits, M, V, ldd, 8));
     LMH_TRY(check_matrix(W, V, K, ldw, 8));
@@ -477,29 +554,35 @@ int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t
         return LMH_ERR_ALIGN;
     if (workspace_bytes < need)
         return LMH_ERR_SHAPE;
-    const Span so = span_of(dX, M, K, ldx, osz);
-    const Span sd = span_of(dlogits, M, V, ldd, 2), sw = span_of(W, V, K, ldw, 2);
     Span ws;
     ws.lo = reinterpret_cast<uintptr_t>(workspace);
     ws.hi = ws.lo + static_cast<uintptr_t>(need);
-    if (overlaps(so, sd) || overlaps(so, sw) || overlaps(ws, so) || overlaps(ws, sd) ||
-        overlaps(ws, sw))
+    if (overlaps(ws, span_of(dX, M, K, ldx, dx_dtype == LMH_FP32 ? 4 : 2)) ||
+        overlaps(ws, span_of(dlogits, M, V, ldd, 2)) || overlaps(ws, span_of(W, V, K, ldw, 2)))
         return LMH_ERR_ALIAS;
-    if (!gemm_grid_fits(K, M, true))
+    LMH_TRY(check_dgrad_split(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V));
+    return launch_dgrad_split(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V, splits,
+                              static_cast<float *>(workspace), stream);
+}
+
+int32_t lmhead_dgrad_noalloc(const void *dlogits, int64_t ldd, const void *W, int64_t ldw,
+                             void *dX, int64_t ldx, int32_t dx_dtype, int64_t M, int64_t K,
+                             int64_t V, int32_t splits, void *stream)
+{
+    LMH_TRY(check_dtype_out(dx_dtype));
+    if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim || splits < 0 ||
+        splits > kMaxSplits)
         return LMH_ERR_SHAPE;
-    lmh::GemmProblem p;
-    p.A = static_cast<const uint16_t *>(W);
-    p.lda = ldw;
-    p.B = static_cast<const uint16_t *>(dlogits);
-    p.ldb = ldd;
-    p.D = dX;
-    p.ldd = ldx;
-    p.R = K;
-    p.C = M;
-    p.P = V;
-    return launch_status(lmh::launch_gemm_dgrad_split(p, dx_dtype != LMH_FP32, splits,
-                                                      static_cast<float *>(workspace),
-                                                      static_cast<hipStream_t>(stream)));
+    const int64_t need = 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
+    if (need == 0)
+        return lmhead_dgrad(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V, stream);
+    if (need > kScratchBytes)
+        return LMH_ERR_SCRATCH;
+    LMH_TRY(check_dgrad_split(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V));
+    void *ws = nullptr;
+    LMH_TRY(scratch_device_address(&ws));
+    return launch_dgrad_split(dlogits, ldd, W, ldw, dX, ldx, dx_dtype, M, K, V, splits,
+                              static_cast<float *>(ws), stream);
 }
 
 int32_t lmhead_wgrad(const void *dlogits, int64_t ldd, const void *x, int64_t ldx, float *dW,

@@ -48,9 +48,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert lmh.lmhead_version() == 103
+    assert lmh.lmhead_version() == 104
     assert lmh.lmhead_status_str(0) == "LMH_OK"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert lmh.lmhead_status_str(s).startswith("LMH_ERR_")
     assert "unknown" in lmh.lmhead_status_str(99)
 
@@ -292,6 +292,28 @@ def test_gemm_grid_limits(L):
     assert need == 2 * (1 << 34) * 4
     assert L.lmhead_dgrad_ws(X, 1 << 13, Y, 1 << 17, Z, 1 << 17, FP32, 1 << 17, 1 << 17,
                              1 << 13, 2, WS, need, None) == SHAPE
+
+
+def test_dgrad_noalloc_validation(L):
+    """The no-allocation dgrad checks on the host like lmhead_dgrad_ws, and
+    refuses a split whose partials exceed its fixed 64 MiB array
+    (LMH_ERR_SCRATCH = 7) before any HIP call."""
+    f = L.lmhead_dgrad_noalloc
+    SCRATCH = 7
+    assert lmh.DGRAD_NOALLOC_MAX_BYTES == 64 << 20
+    assert f(A, 1000, B, 64, C, 64, FP16, 16, 64, 1000, 2, None) == DTYPE
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 17, None) == SHAPE
+    assert f(A, 1000, B, 64, C, 64, FP32, 16, 64, 1000, -1, None) == SHAPE
+    assert f(A, 1000, B, 64, A + 64, 64, FP32, 16, 64, 1000, 2, None) == ALIAS
+    assert f(A + 8, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, None) == ALIGN
+    assert f(None, 1000, B, 64, C, 64, FP32, 16, 64, 1000, 2, None) == NULL
+    # 4 parts of 1024 x 8192 FP32 partials: 128 MiB > 64 MiB
+    assert f(A, 32768, B, 8192, C, 8192, BF16, 1024, 8192, 32768, 4, None) == SCRATCH
+    # the default split of that shape fills the array exactly: not refused
+    # for size (the call would run, so it is not made here)
+    assert L.lmhead_dgrad_workspace_bytes(1024, 8192, 32768, 0) == 64 << 20
+    # unsplit shapes are lmhead_dgrad, with its checks
+    assert f(A, 120, B, 64, C, 64, BF16, 16, 64, 128, 1, None) == SHAPE      # ldd < V
 
 
 def test_diag_mfma_loop_validation(L):
