@@ -141,12 +141,14 @@ __device__ __forceinline__ void merge_md(float &m, float &d, float m2, float d2)
 }
 
 // FP32 -> BF16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+// Written as a select (no branch), so that per-element use compiles to
+// straight-line code.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x40u;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded;
 }
 
 }  // namespace lmh

@@ -71,6 +71,43 @@ __device__ __forceinline__ float max4(const float4 &v)
     return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
 }
 
+// The single-read kernels keep each value's exponential: v <- exp(v - m_t)
+// (and the tail value when present), d += every one of them, with m_t the
+// thread's own maximum; when m_t = -inf every value is -inf and every e is 0.
+// The gradient then needs one multiply per value: exp(z - m) dloss / d =
+// e * grad_scale, grad_scale = exp(m_t - m) * dloss / d.
+template <int PER>
+__device__ __forceinline__ void exp_in_place(float4 (&v)[PER], float &tv, bool has_tail,
+                                             float m_t, float &d)
+{
+    const float ms = (m_t == -INFINITY) ? 0.0f : m_t;  // exp2(-inf) = 0 for every value
+    float acc = 0.0f;
+    if (has_tail) {
+        tv = exp_shifted(tv, ms);
+        acc = tv;
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        v[p].x = exp_shifted(v[p].x, ms);
+        v[p].y = exp_shifted(v[p].y, ms);
+        v[p].z = exp_shifted(v[p].z, ms);
+        v[p].w = exp_shifted(v[p].w, ms);
+        acc += v[p].x;
+        acc += v[p].y;
+        acc += v[p].z;
+        acc += v[p].w;
+    }
+    d = acc;
+}
+
+__device__ __forceinline__ float grad_scale(float m_t, float m, float d, float up, bool bad)
+{
+    if (bad)
+        return __int_as_float(0x7fc00000);
+    const float rescale = (m_t == -INFINITY) ? 0.0f : exp_shifted(m_t, m);
+    return rescale * (up / d);
+}
+
 // Reduce columns [0, ncols) of one row (16-byte aligned start) to the pair
 // (m, d) = (max z, sum exp(z - m)); the result is valid in thread 0.  Each
 // thread keeps a running pair over U 16-byte loads at a time (one rescale per
@@ -404,22 +441,17 @@ __global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t 
         v[p] = (i < n4) ? ld4<true>(z4 + i)
                         : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
-    const float tv = has_tail ? zr[jt] : -INFINITY;
+    float tv = has_tail ? zr[jt] : -INFINITY;
 
+    // Per thread: m_t = its max, e = exp(z - m_t) kept in place of z, d_t =
+    // sum of e (all zero when every value is -inf).
     float m = tv;
 #pragma unroll
     for (int p = 0; p < PER; ++p)
         m = fmaxf(m, max4(v[p]));
-    float d = has_tail ? exp_shifted(tv, m) : 0.0f;
-    if (m != -INFINITY) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            d += exp_shifted(v[p].x, m);
-            d += exp_shifted(v[p].y, m);
-            d += exp_shifted(v[p].z, m);
-            d += exp_shifted(v[p].w, m);
-        }
-    }
+    const float m_t = m;
+    float d = 0.0f;
+    exp_in_place(v, tv, has_tail, m_t, d);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float m2 = __shfl_xor(m, off, 64);
@@ -463,13 +495,13 @@ __global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t 
     m = row_m;
     d = row_d;
     const float up = ignored ? 0.0f : dloss[dloss_stride * row];
-    const float coef = bad ? __int_as_float(0x7fc00000) : up / d;
+    // exp(z - m) / d * dloss = e * exp(m_t - m) * dloss / d
+    const float scale = grad_scale(m_t, m, d, up, bad);
 
-    auto grad = [&](float zv, int64_t j) {
+    auto grad = [&](float e, int64_t j) {
         if (ignored)
             return 0.0f;
-        const float e = exp_shifted(zv, m);
-        return (j == static_cast<int64_t>(y)) ? fmaf(e, coef, -up) : e * coef;
+        return (j == static_cast<int64_t>(y)) ? fmaf(e, scale, -up) : e * scale;
     };
 #pragma unroll
     for (int p = 0; p < PER; ++p) {

@@ -551,12 +551,16 @@ def test_split_merge_nan_rows():
 @pytest.mark.parametrize("n,V,mode", [(1, 1, "scalar"), (3, 5, "per_row"), (33, 65, "scalar"),
                                       (600, 4097, "per_row"), (128, 32768, "scalar"),
                                       (5, 40001, "per_row"), (7, 65536, "scalar"),
-                                      (3, 65537, "per_row")])
+                                      (3, 65537, "per_row"),
+                                      # several rounds of workgroups per CU
+                                      (600, 32768, "per_row"), (520, 16384, "scalar"),
+                                      (1024, 32768, "scalar")])
 def test_fused_matches_oracle(n, V, mode):
     """Stats and gradients of the one-read kernel against the oracle: 8 and 16
     float4 per thread, ragged tails, ignored rows, scalar and per-row dloss,
-    rows past 65536 columns (the two-kernel path); BF16 == RNE(FP32);
-    in place == out of place bitwise; agrees with fwd + bwd to rounding."""
+    rows past 65536 columns (the two-kernel path), 520 - 1024 rows of 16384
+    and 32768 columns; BF16 == RNE(FP32); in place == out of place bitwise;
+    agrees with fwd + bwd to rounding."""
     inp = workloads.xent_logits(n, V, sigma=2.5, spike_frac=0.1, spike=30.0, ignore_frac=0.15,
                                 seed=n * 7 + V)
     _say(f"fused n={n} V={V} {mode}")
