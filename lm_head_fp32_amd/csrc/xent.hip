@@ -533,14 +533,19 @@ __global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t 
 
 constexpr int kMeanThreads = 1024;
 
+// Mean of the valid rows' losses and 1/n_valid, in FP64, one workgroup:
+// thread t sums rows t, t + 1024, ... in order; each wave combines its 64
+// partial sums by a butterfly, and thread 0 adds the 16 wave sums in wave
+// order.  A fixed order throughout, so the result is deterministic.
 __global__ __launch_bounds__(kMeanThreads) void xent_mean_kernel(const float *__restrict__ loss,
                                                                  const int32_t *__restrict__ tgt,
                                                                  int32_t ignore_index, int64_t n,
                                                                  float *mean_out, float *inv_out)
 {
+    constexpr int NW = kMeanThreads / 64;
     const int tid = threadIdx.x;
     double s = 0.0;
-    long long c = 0;
+    int64_t c = 0;
     for (int64_t i = tid; i < n; i += kMeanThreads) {
         if (tgt[i] != ignore_index) {
             if (loss)  // NULL: count only (1 / n_valid)
@@ -548,22 +553,27 @@ __global__ __launch_bounds__(kMeanThreads) void xent_mean_kernel(const float *__
             ++c;
         }
     }
-    __shared__ double ss[kMeanThreads];
-    __shared__ long long sc[kMeanThreads];
-    ss[tid] = s;
-    sc[tid] = c;
-    __syncthreads();
-    for (int w = kMeanThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) {
-            ss[tid] += ss[tid + w];
-            sc[tid] += sc[tid + w];
-        }
-        __syncthreads();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        s += __shfl_xor(s, off, 64);
+        c += __shfl_xor(c, off, 64);
     }
+    __shared__ double ws[NW];
+    __shared__ int64_t wc[NW];
+    if ((tid & 63) == 0) {
+        ws[tid >> 6] = s;
+        wc[tid >> 6] = c;
+    }
+    __syncthreads();
     if (tid == 0) {
-        const long long nv = sc[0];
+        double sum = 0.0;
+        int64_t nv = 0;
+        for (int w = 0; w < NW; ++w) {
+            sum += ws[w];
+            nv += wc[w];
+        }
         if (mean_out)
-            *mean_out = nv ? static_cast<float>(ss[0] / static_cast<double>(nv)) : 0.0f;
+            *mean_out = nv ? static_cast<float>(sum / static_cast<double>(nv)) : 0.0f;
         if (inv_out)
             *inv_out = nv ? static_cast<float>(1.0 / static_cast<double>(nv)) : 0.0f;
     }
