@@ -65,9 +65,12 @@ PEAK_HBM_GBS = 8000.0
 # counters on this GPU), valid only for the kernel sources they were taken on
 # (code hash of the .hip file, see source_code_hash).  Changed code reports null.
 MEASURED_TRAFFIC = {
-    "logits_fp32": {"src": "gemm.hip", "sha": "5fba6e9415ffeb18", "bytes": (2 * 395964 + 131088) * 1024},
-    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "90e3a3bef99ccf2c",
-                          "bytes": (2 * 2097954 + 513 + 2 * 2056476 + 4195363) * 1024},
+    "logits_fp32": {"src": "gemm.hip", "sha": "5fba6e9415ffeb18",
+                    "bytes": int((2 * 395972.8 + 131078.9) * 1024)},
+    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "ea1a23b513ff0282",
+                          "bytes": int((2 * 2097959.4 + 513.5 + 2 * 2056473.4 + 4195416.0) * 1024)},
+    "xent_fused_bf16_1024x32768": {"src": "xent.hip", "sha": "ea1a23b513ff0282",
+                                   "bytes": int((2 * 65695.6 + 65604.5) * 1024)},
 }
 
 
@@ -621,6 +624,8 @@ def main():
     ce_one_bytes = 4.0 * M * V + 2.0 * M * V + 24 * M
     kern["xent_fused"]["gbps"] = ce_one_bytes / (kern["xent_fused"]["ms_mean"] * 1e-3) / 1e9
     kern["xent_fused"]["frac_hbm_peak"] = kern["xent_fused"]["gbps"] / PEAK_HBM_GBS
+    kern["xent_fused"]["algorithmic_bytes"] = int(ce_one_bytes)
+    kern["xent_fused"]["traffic"] = measured_traffic("xent_fused_bf16_1024x32768")
     logits_tflops = kern["logits"]["tflops"]
     log(f"[bench] step {ms_step:.3f} ms; logits {kern['logits']['ms_mean']:.3f} ms "
         f"= {logits_tflops:.1f} TFLOPS; CE (one read) {kern['xent_fused']['ms_mean'] * 1e3:.1f} us")
