@@ -17,6 +17,10 @@
 // Kernels:
 //  * gemm_pp -- the logits GEMM with many tokens and K <= 8192: 256 x 256
 //    tiles, two wave groups one phase apart over a four-stage LDS ring.
+//  * gemm_wgp -- wgrad over whole tiles: persistent, the next tile's loads
+//    and MFMAs overlapping the finished tile's dW stores.
+//  * gemm_wg2 -- wgrad for few tokens otherwise: 256 x 128 tiles, two
+//    workgroups per CU.
 //  * gemm_big -- 256 x 256 / 256 x 128 / 128 x 128 tiles, two LDS stages fed
 //    by direct buffer loads; the logits GEMM for longer K, and dgrad and wgrad
 //    (p-major operands read through transposing LDS loads).
@@ -1694,6 +1698,256 @@ hipError_t launch_wg2(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// gemm_wgp: persistent wgrad over whole 256 x 256 tiles (K and V multiples of
+// 256, M a multiple of 128), the FP32 store epilogue.  dW is the largest
+// output of the step (V x K FP32), and a tile's 256 KiB of stores take
+// several microseconds to drain; here they overlap the next tile's work:
+//  * one 8-wave workgroup per CU (128 KiB of stage buffers + a 32 KiB
+//    epilogue area) walks its XCD's share of the tiles in order, so the
+//    next tile's first two 64-deep stages are loaded while the finished tile
+//    is written out;
+//  * each wave writes its 64 x 128 block through a private 4 KiB LDS area,
+//    one 32 x 32 fragment at a time (four row-major 16-byte writes, then
+//    eight whole 128-byte rows per store instruction), with no workgroup
+//    barrier, so the stores stay in flight into the next tile;
+//  * only the four waves of wave column 0 issue the direct loads (16 per
+//    stage each) and wait on them: vmcnt retires a wave's loads and stores in
+//    issue order, so a wait on a stage also waits on that wave's earlier
+//    stores, and the other four waves' stores never hold up a stage.
+// Stage s of a tile sits in LDS buffer s % 2 (the stage count is even, so
+// every tile starts in buffer 0).  Loads are issued from inline assembly,
+// untracked by the compiler; the waits count them exactly.  Same operand
+// layout, MFMA order and accumulation order as gemm_big's 256 x 256 tile, so
+// the two give bitwise-identical dW.
+__device__ __forceinline__ int wgp_swz(int row)
+{
+    // 16-byte chunk key of a 128-byte row: distinct over any 8 consecutive
+    // rows, and (chunk, row parity) distinct over any 16.
+    return (row & 7) ^ ((row >> 3) & 1);
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_wgp(GemmProblem g, TileMap tm, int per_xcd)
+{
+    constexpr int BR = 256, BC = 256, BK = 64, WR = 4, NL = 4;
+    constexpr int TR = 64, TC = 128, FR = TR / 32, FC = TC / 32;
+    using OpA = TrOperand<BR, BK, NL>;  // x [M][K]: rows r = k
+    using OpB = TrOperand<BC, BK, NL>;  // dlogits [M][V]: rows c = v
+    constexpr int NDMA = OpA::NB + OpB::NB;  // direct loads per loading wave per stage
+    constexpr int NST = FR * FC * 4;          // stores per wave per tile
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[BR * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA1[BR * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[BC * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB1[BC * BK];
+    __shared__ __attribute__((aligned(16))) float sE[8 * 32 * 32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % WR;
+    const int wc = wave / WR;
+    const bool loads = wc == 0;
+    // Workgroups b, b + 8, ... share an XCD; XCD x takes the tiles
+    // [x per_xcd, (x + 1) per_xcd) of the grouped order, gridDim.x / 8 at a
+    // time.
+    const int xcd = blockIdx.x % kXcds;
+    const int slots = gridDim.x / kXcds;
+    auto decode = [&](int j, int64_t &r0, int64_t &c0) {
+        const int v = xcd * per_xcd + j;
+        const int gsz = tm.group_r * tm.tiles_c;
+        const int gi = v / gsz;
+        const int first_r = gi * tm.group_r;
+        const int rows_in_group = min(tm.tiles_r - first_r, tm.group_r);
+        const int in = v - gi * gsz;
+        r0 = static_cast<int64_t>(first_r + in % rows_in_group) * BR;
+        c0 = static_cast<int64_t>(in / rows_in_group) * BC;
+    };
+
+    OpA opA;
+    OpB opB;
+    opA.init(g.A, g.lda, 0, g.R, g.P, wr, lane, wr * TR);
+    opB.init(g.B, g.ldb, 0, g.C, g.P, wr, lane, wc * TC);
+    // Stage kt of the tile at (r0, c0) into (lA, lB), by the loading waves.
+    auto dma = [&](uint16_t *lA, uint16_t *lB, int64_t r0, int64_t c0, int64_t kt) {
+        if (!loads)
+            return;
+        const __amdgpu_buffer_rsrc_t ra = tile_rsrc(g.A + kt * BK * g.lda + r0);
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(g.B + kt * BK * g.ldb + c0);
+#pragma unroll
+        for (int i = 0; i < OpA::NB; ++i)
+            dma16_untracked(ra, lds_addr(lA + (wr * OpA::NB + i) * 512), opA.off[i], 0);
+#pragma unroll
+        for (int i = 0; i < OpB::NB; ++i)
+            dma16_untracked(rb, lds_addr(lB + (wr * OpB::NB + i) * 512), opB.off[i], 0);
+    };
+
+    bf16x8 fa[2][FR], fb[2][FC];
+    auto frag_load = [&](const uint16_t *lA, const uint16_t *lB, int kk, int sl) {
+#pragma unroll
+        for (int i = 0; i < FR; ++i)
+            fa[sl][i] = opA.frag(lA, i, kk);
+#pragma unroll
+        for (int j = 0; j < FC; ++j)
+            fb[sl][j] = opB.frag(lB, j, kk);
+    };
+    f32x16 acc[FR][FC];
+    auto mfma_rows = [&](int sl, int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < FC; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j],
+                                                                    acc[i][j], 0, 0, 0);
+    };
+    // The MFMAs of one stage whose k-step-0 fragments are in slot 0, fragment
+    // reads one k step ahead; the last half row of MFMAs is left to the
+    // caller, to run behind its wait and barrier.
+    auto stage_mfma = [&](const uint16_t *cA, const uint16_t *cB) {
+        frag_load(cA, cB, 1, 1);
+        mfma_rows(0, 0, FR);
+        frag_load(cA, cB, 2, 0);
+        mfma_rows(1, 0, FR);
+        frag_load(cA, cB, 3, 1);
+        mfma_rows(0, 0, FR);
+        mfma_rows(1, 0, FR / 2);
+    };
+    // Hand-off between stages: the loading waves wait until at most N of
+    // their memory operations are in flight, then every wave's LDS reads are
+    // done and the workgroup meets.
+    auto hand_off = [&](auto nc) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (loads)
+            vm_wait<decltype(nc)::value>();
+        pp_barrier();
+    };
+
+    const int cl = lane & 31, hl = lane >> 5;
+    float *const own = sE + wave * 32 * 32;
+    auto epilogue = [&](int64_t r0, int64_t c0) {
+#pragma unroll
+        for (int t = 0; t < FC; ++t)
+#pragma unroll
+            for (int i = 0; i < FR; ++i) {
+                // Lane (cl, hl) holds rows 8q + 4hl .. + 3 of output row cl.
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float4 v;
+                    v.x = acc[i][t][4 * q + 0];
+                    v.y = acc[i][t][4 * q + 1];
+                    v.z = acc[i][t][4 * q + 2];
+                    v.w = acc[i][t][4 * q + 3];
+                    *reinterpret_cast<float4 *>(&own[cl * 32 + (((2 * q + hl) ^ wgp_swz(cl)) << 2)]) =
+                        v;
+                }
+                // Eight lanes per 128-byte row, eight rows per store.
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int rr = 8 * s + (lane >> 3), kc = lane & 7;
+                    const float4 v =
+                        *reinterpret_cast<const float4 *>(&own[rr * 32 + ((kc ^ wgp_swz(rr)) << 2)]);
+                    float *out = static_cast<float *>(g.D) + (c0 + wc * TC + t * 32 + rr) * g.ldd +
+                                 r0 + wr * TR + i * 32 + 4 * kc;
+                    store16(out, v, true);
+                }
+            }
+    };
+
+    const int64_t nk = g.P / BK;  // even, >= 2
+    int j = blockIdx.x / kXcds;
+    if (j >= per_xcd)
+        return;
+    int64_t r0, c0;
+    decode(j, r0, c0);
+    // In flight at the top of a tile, in issue order: stage 0 (NDMA), stage 1
+    // (NDMA) and, after the first tile, the previous tile's NST stores.
+    dma(sA0, sB0, r0, c0, 0);
+    dma(sA1, sB1, r0, c0, 1);
+    bool first = true;
+    for (;;) {
+        const std::integral_constant<int, NDMA> after_s0_first;
+        const std::integral_constant<int, NDMA + NST> after_s0;
+        if (first)
+            hand_off(after_s0_first);
+        else
+            hand_off(after_s0);
+#pragma unroll
+        for (int i = 0; i < FR; ++i)
+#pragma unroll
+            for (int jx = 0; jx < FC; ++jx)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[i][jx][e] = 0.0f;
+        frag_load(sA0, sB0, 0, 0);
+        const int jn = j + slots;
+        const bool has_next = jn < per_xcd;
+        int64_t nr0 = 0, nc0 = 0;
+        if (has_next)
+            decode(jn, nr0, nc0);
+        // Stage 0 (buffer 0); stage 1 is already on its way into buffer 1.
+        stage_mfma(sA0, sB0);
+        const std::integral_constant<int, 0> none;
+        const std::integral_constant<int, NST> after_s1;
+        if (first)
+            hand_off(none);
+        else
+            hand_off(after_s1);
+        frag_load(sA1, sB1, 0, 0);
+        mfma_rows(1, FR / 2, FR);
+        // Stages 1 .. nk - 2 in pairs: each loads the stage after it into the
+        // buffer the previous stage freed.
+        int64_t kt = 1;
+        for (; kt + 2 < nk; kt += 2) {
+            dma(sA0, sB0, r0, c0, kt + 1);
+            stage_mfma(sA1, sB1);
+            hand_off(none);
+            frag_load(sA0, sB0, 0, 0);
+            mfma_rows(1, FR / 2, FR);
+            dma(sA1, sB1, r0, c0, kt + 2);
+            stage_mfma(sA0, sB0);
+            hand_off(none);
+            frag_load(sA1, sB1, 0, 0);
+            mfma_rows(1, FR / 2, FR);
+        }
+        // Last stage (buffer 1): the next tile's stage 0 goes into buffer 0
+        // now, its stage 1 into buffer 1 once every wave has read it.
+        if (has_next)
+            dma(sA0, sB0, nr0, nc0, 0);
+        stage_mfma(sA1, sB1);
+        mfma_rows(1, FR / 2, FR);
+        pp_barrier();
+        if (has_next)
+            dma(sA1, sB1, nr0, nc0, 1);
+        epilogue(r0, c0);
+        if (!has_next)
+            break;
+        j = jn, r0 = nr0, c0 = nc0;
+        first = false;
+    }
+}
+
+// gemm_wgp's shapes: whole tiles, an even number of 64-deep stages, and at
+// least two tiles per CU in whole groups of eight (one range per XCD).
+bool wgp_fits(const GemmProblem &p)
+{
+    if (p.psplit != 0 || p.R % 256 != 0 || p.C % 256 != 0 || p.P % 128 != 0 || p.P == 0)
+        return false;
+    const int64_t tiles = (p.R / 256) * (p.C / 256);
+    return tiles >= 512 && tiles % kXcds == 0;
+}
+
+hipError_t launch_wgp(const GemmProblem &p, int group_r, hipStream_t s)
+{
+    TileMap tm;
+    tm.tiles_r = static_cast<int>(p.R / 256);
+    tm.tiles_c = static_cast<int>(p.C / 256);
+    tm.group_r = std::min(std::max(group_r, 1), tm.tiles_r);
+    const int per_xcd = tm.tiles_r * tm.tiles_c / kXcds;
+    // One workgroup per CU (160 KiB of LDS each).
+    hipLaunchKernelGGL(gemm_wgp, dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+    return hipGetLastError();
+}
+
 template <int BR, int BC, int WR, int WC, bool AT, bool BT>
 hipError_t launch_big(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
@@ -1867,6 +2121,16 @@ hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
 #define LMH_WGRAD_WG2 512
 #endif
     if constexpr (AT && BT) {
+        // Whole-tile wgrad with the store epilogue: the persistent kernel,
+        // whose dW stores overlap the next tile.  Measured on MI355X against
+        // the kernels below (bitwise-identical dW), K=8192 V=32768: M=128
+        // 197-215 -> 184-189 us, M=256 259 -> 199-208, M=512 365-369 ->
+        // 304-305, M=768 485-488 -> 411-418, M=1024 573-575 -> 514-516,
+        // M=4096 1784-1809 -> 1755-1770; K=16384 V=131072: M=128 1477-1594 ->
+        // 1427, M=512 2918-3000 -> 2365-2373, M=4096 14217-14241 ->
+        // 13687-13760 us.
+        if (epi == Epi::kStoreF32 && wgp_fits(p))
+            return launch_wgp(p, wgrad_group, s);
         if (p.P <= LMH_WGRAD_WG2 && tiles256x128 >= 512)
             return launch_wg2(p, epi, wgrad_group, s);
     }

@@ -370,6 +370,52 @@ def test_wgrad_random_sampled():
     assert_gemm_close(host_f32(dw)[rows], ref, S, 1e-5, "wgrad")
 
 
+# wgrad over whole tiles with the store epilogue runs the persistent kernel:
+# one workgroup per CU walking its XCD's tiles, the next tile's first two
+# stages loaded while the finished tile is stored.  Cases: two stages (the
+# least, M=128), three stage pairs (M=384), uneven tiles per workgroup (520
+# tiles: 65 per XCD over 32 workgroups), a padded dW pre-filled with NaN.
+@pytest.mark.parametrize("M,K,V", [(128, 2048, 16640), (384, 4096, 8192)])
+def test_wgrad_persistent_integer_exact(M, K, V):
+    dl_bits, x_bits = workloads.integer_operands([(M, V), (M, K)], seed=7000 + M)
+    _say(f"wgrad persistent int M={M} K={K} V={V}")
+    dl, x = dev_bf16(dl_bits), dev_bf16(x_bits)
+    dw = padded_out(V, K, K + 4, torch.float32)
+    lmh.lmhead_wgrad(dl, x, dW=dw)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dw).any().item()
+    assert padding_untouched(dw)
+    if M == 128:
+        ref, _ = oracle.wgrad(dl_bits, x_bits)          # every element
+        assert np.array_equal(_f32_bits(host_f32(dw)), _f32_bits(ref.astype(np.float32)))
+    else:
+        rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(V - 300, V),
+                                         np.random.default_rng(M).integers(0, V, 200)]))
+        ref, _ = oracle.wgrad(dl_bits, x_bits, rows=rows)
+        got = host_f32(dw[torch.from_numpy(rows).cuda()])
+        assert np.array_equal(_f32_bits(got), _f32_bits(ref.astype(np.float32)))
+
+
+def test_wgrad_persistent_matches_accumulate_path():
+    """Random BF16 operands at M=1024 K=8192 V=32768: the store path (the
+    persistent kernel) and accumulation into zeros (gemm_big's 256 x 256
+    tile) sum in the same order, so dW agrees bitwise everywhere; sampled
+    rows against the oracle."""
+    rng = np.random.default_rng(workloads.SEED + 71)
+    dl_bits = workloads.normal_bf16(rng, (1024, 32768), 1e-3)
+    x_bits = workloads.normal_bf16(rng, (1024, 8192), 1.0)
+    _say("wgrad persistent vs accumulate 1024x8192x32768")
+    dl, x = dev_bf16(dl_bits), dev_bf16(x_bits)
+    dw = lmh.lmhead_wgrad(dl, x)
+    dz = torch.zeros_like(dw)
+    lmh.lmhead_wgrad(dl, x, dW=dz, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), dz.view(torch.int32))
+    rows = np.array([0, 255, 256, 8191, 16384, 32767])
+    ref, S = oracle.wgrad(dl_bits, x_bits, rows=rows)
+    assert_gemm_close(host_f32(dw)[rows], ref, S, 1e-5, "wgrad")
+
+
 # ------------------------------------------- steady-state paths, integer exact
 
 def test_logits_integer_exact_interior_tiles():
@@ -400,9 +446,9 @@ def test_dgrad_integer_exact_interior_tiles():
 
 
 def test_wgrad_integer_exact_interior_tiles():
-    """M=2048 K=4096 V=8192: wgrad runs 256x256 8-wave tiles with both
-    p-major operands read through transposing LDS loads; sampled rows
-    bit-exact, then accumulate."""
+    """M=2048 K=4096 V=8192: wgrad's 256x256 8-wave tiles (the persistent
+    kernel; accumulate runs gemm_big) with both p-major operands read through
+    transposing LDS loads; sampled rows bit-exact, then accumulate."""
     dl_bits, x_bits = workloads.integer_operands([(2048, 8192), (2048, 4096)], seed=43)
     _say("wgrad int interior 2048x4096x8192")
     dl, x = dev_bf16(dl_bits), dev_bf16(x_bits)
