@@ -15,14 +15,15 @@
 // whole rows.
 //
 // Kernels:
-//  * gemm_pp -- the logits GEMM with many tokens and K <= 8192: 256 x 256
-//    tiles, two wave groups one phase apart over a four-stage LDS ring.
+//  * gemm_pp -- the logits GEMM with many tokens and K <= 2048 (or at most
+//    384 tokens): 256 x 256 tiles, two wave groups one phase apart over a
+//    four-stage LDS ring.
 //  * gemm_wgp -- wgrad over whole tiles: persistent, the next tile's loads
 //    and MFMAs overlapping the finished tile's dW stores.
 //  * gemm_wg2 -- wgrad for few tokens otherwise: 256 x 128 tiles, two
 //    workgroups per CU.
 //  * gemm_big -- 256 x 256 / 256 x 128 / 128 x 128 tiles, two LDS stages fed
-//    by direct buffer loads; the logits GEMM for longer K, and dgrad and wgrad
+//    by direct buffer loads; the logits GEMM for K >= 4096, and dgrad and wgrad
 //    (p-major operands read through transposing LDS loads).
 //  * gemm_small -- the logits GEMM for few tokens (W streamed once).
 //  * gemm_rows -- the logits GEMM for at most 16 tokens and K >= 8192: W
@@ -960,9 +961,15 @@ gemm_big(GemmProblem gp, TileMap tm)
         frag_load(sA0, sB0, 0, 0);
     }
     if (interior) {
-        for (; kt + 3 < nfull; kt += 2) {
+        for (; kt + 3 <= nfull; kt += 2) {
             stage_fast(sA0, sB0, sA1, sB1, kt);
             stage_fast(sA1, sB1, sA0, sB0, kt + 1);
+        }
+        // One more (stage kt is in buffer 0) when the next stage is full, so
+        // that only the last full stage is computed without a load behind it.
+        if (kt + 1 < nfull) {
+            stage_fast(sA0, sB0, sA1, sB1, kt);
+            ++kt;
         }
     }
     // Remaining stages (all of them for an edge tile): guarded register loads
@@ -2071,12 +2078,19 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
                            : launch_small<64, 6>(p, epi, 8, s);
     if (p.C <= 256)
         return launch_small<128, LMH_SMALL_S128>(p, epi, 8, s);
-    // Many tokens: the ping-pong ring kernel for K <= 8192 (measured 1-3 %
-    // ahead of gemm_big there on MI355X), gemm_big for longer K (2-5 % ahead).
+    // Many tokens: the ping-pong ring kernel for K <= 2048 or at most 384
+    // tokens, gemm_big otherwise.  Measured on MI355X (V=32768, medians of 15,
+    // three alternated rounds), gemm_pp -> gemm_big: M=1024 K=1024 79.6-80.6
+    // -> 82.0-83.1 us, K=2048 126.6-138.7 -> 128.1-143.1, K=4096 240.6-249.5
+    // -> 229.6-241.3, K=8192 482.6-490.4 -> 463.7-469.9; M=384 K=8192
+    // 230.2-235.0 -> 237.2-242.2; M=512 K=4096 133.5-134.7 -> 129.8-130.2;
+    // M=2048 K=4096 460.7-470.6 -> 455.1-461.8; M=4096 K=8192 1878-1882 ->
+    // 1825-1839; M=1024 K=8192 V=131072 1899-1932 -> 1850-1865.
 #ifndef LMH_PP
 #define LMH_PP 1
 #endif
-    if (LMH_PP && p.P % 32 == 0 && p.P <= 8192 && epi != Epi::kAccumF32)
+    if (LMH_PP && p.P % 32 == 0 && (p.P <= 2048 || (p.C <= 384 && p.P <= 8192)) &&
+        epi != Epi::kAccumF32)
         return launch_pp(p, epi, 8, s);
     return launch_big<256, 256, 4, 2, false, false>(p, epi, 8, s);
 }
