@@ -2271,9 +2271,16 @@ hipError_t launch_gemm_dgrad_split(const GemmProblem &p, bool bf16_out, int spli
     const int ns = static_cast<int>((p.P + q.psplit - 1) / q.psplit);
     if (!big_offsets_fit(q))
         return launch_gemm_dgrad(p, bf16_out ? Epi::kStoreBF16 : Epi::kStoreF32, s);
-    const hipError_t e = p.C <= 128
-                             ? launch_big<256, 128, 4, 2, true, false>(q, Epi::kStoreF32, 8, s)
-                             : launch_big<256, 256, 4, 2, true, false>(q, Epi::kStoreF32, 8, s);
+    // Tile order: 2 tile rows (K) walked before stepping along M, so the
+    // tiles that share a W strip run on one XCD.  Measured on MI355X against
+    // 8 (bitwise-identical dX, three alternated rounds of 15): M=512 K=8192
+    // V=32768 261-318 -> 243-262 us, M=1024 452-519 -> 447-485, M=128 K=4096
+    // 70.1-71.4 -> 68.2-69.8, M=512 K=16384 V=131072 1778-1804 -> 1766-1772,
+    // M=256 within 1 %; 4 was within 1 % of 2, 16 slower.
+    constexpr int kSplitGroup = 2;
+    const hipError_t e =
+        p.C <= 128 ? launch_big<256, 128, 4, 2, true, false>(q, Epi::kStoreF32, kSplitGroup, s)
+                   : launch_big<256, 256, 4, 2, true, false>(q, Epi::kStoreF32, kSplitGroup, s);
     if (e != hipSuccess)
         return e;
     const int64_t nthr = p.C * (R4 / 4);
