@@ -18,8 +18,9 @@
 //  * gemm_pp -- the logits GEMM with many tokens and K <= 2048 (or at most
 //    384 tokens): 256 x 256 tiles, two wave groups one phase apart over a
 //    four-stage LDS ring.
-//  * gemm_wgp -- wgrad over whole tiles: persistent, the next tile's loads
-//    and MFMAs overlapping the finished tile's dW stores.
+//  * gemm_persist -- wgrad and the many-token logits GEMM over whole tiles:
+//    persistent, the next tile's loads and MFMAs overlapping the finished
+//    tile's stores.
 //  * gemm_wg2 -- wgrad for few tokens otherwise: 256 x 128 tiles, two
 //    workgroups per CU.
 //  * gemm_big -- 256 x 256 / 256 x 128 / 128 x 128 tiles, two LDS stages fed
@@ -1706,18 +1707,19 @@ hipError_t launch_wg2(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// gemm_wgp: persistent wgrad over whole 256 x 256 tiles (K and V multiples of
-// 256, M a multiple of 128), the FP32 store epilogue.  dW is the largest
-// output of the step (V x K FP32), and a tile's 256 KiB of stores take
-// several microseconds to drain; here they overlap the next tile's work:
+// gemm_persist: persistent GEMM over whole 256 x 256 tiles (R and C multiples
+// of 256, P a multiple of 128) with a store epilogue -- wgrad (TRANS: both
+// operands p-major) and the logits GEMM (both contraction-contiguous).  Each
+// tile's output (256 KiB of FP32) takes several microseconds to drain; here
+// it overlaps the next tile's work:
 //  * one 8-wave workgroup per CU (128 KiB of stage buffers + a 32 KiB
 //    epilogue area) walks its XCD's share of the tiles in order, so the
 //    next tile's first two 64-deep stages are loaded while the finished tile
 //    is written out;
 //  * each wave writes its 64 x 128 block through a private 4 KiB LDS area,
-//    one 32 x 32 fragment at a time (four row-major 16-byte writes, then
-//    eight whole 128-byte rows per store instruction), with no workgroup
-//    barrier, so the stores stay in flight into the next tile;
+//    one 32 x 32 fragment at a time (row-major writes, then whole 128-byte
+//    FP32 or 64-byte BF16 row pieces per store instruction), with no
+//    workgroup barrier, so the stores stay in flight into the next tile;
 //  * only the four waves of wave column 0 issue the direct loads (16 per
 //    stage each) and wait on them: vmcnt retires a wave's loads and stores in
 //    issue order, so a wait on a stage also waits on that wave's earlier
@@ -1725,24 +1727,30 @@ hipError_t launch_wg2(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 // Stage s of a tile sits in LDS buffer s % 2 (the stage count is even, so
 // every tile starts in buffer 0).  Loads are issued from inline assembly,
 // untracked by the compiler; the waits count them exactly.  Same operand
-// layout, MFMA order and accumulation order as gemm_big's 256 x 256 tile, so
-// the two give bitwise-identical dW.
-__device__ __forceinline__ int wgp_swz(int row)
+// layouts, MFMA order and accumulation order as gemm_big's 256 x 256 tile, so
+// the two give bitwise-identical output.
+__device__ __forceinline__ int persist_swz(int row)
 {
     // 16-byte chunk key of a 128-byte row: distinct over any 8 consecutive
     // rows, and (chunk, row parity) distinct over any 16.
     return (row & 7) ^ ((row >> 3) & 1);
 }
 
+template <bool TRANS, int EPI>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_wgp(GemmProblem g, TileMap tm, int per_xcd)
+gemm_persist(GemmProblem g, TileMap tm, int per_xcd)
 {
     constexpr int BR = 256, BC = 256, BK = 64, WR = 4, NL = 4;
     constexpr int TR = 64, TC = 128, FR = TR / 32, FC = TC / 32;
-    using OpA = TrOperand<BR, BK, NL>;  // x [M][K]: rows r = k
-    using OpB = TrOperand<BC, BK, NL>;  // dlogits [M][V]: rows c = v
-    constexpr int NDMA = OpA::NB + OpB::NB;  // direct loads per loading wave per stage
-    constexpr int NST = FR * FC * 4;          // stores per wave per tile
+    constexpr bool BF = EPI == static_cast<int>(Epi::kStoreBF16);
+    static_assert(EPI == static_cast<int>(Epi::kStoreF32) || BF, "store epilogues only");
+    // p-major operands (wgrad: x [M][K], dlogits [M][V]) are read through
+    // transposing LDS loads; contraction-contiguous ones (logits: W [V][K],
+    // x [M][K]) keep gemm_big's k-contiguous stage layout.
+    using OpA = std::conditional_t<TRANS, TrOperand<BR, BK, NL>, DmaOperand<BR, BK, NL>>;
+    using OpB = std::conditional_t<TRANS, TrOperand<BC, BK, NL>, DmaOperand<BC, BK, NL>>;
+    constexpr int NDMA = OpA::NB + OpB::NB;    // direct loads per loading wave per stage
+    constexpr int NST = FR * FC * (BF ? 2 : 4);  // stores per wave per tile
     __shared__ __attribute__((aligned(16))) uint16_t sA0[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB0[BC * BK];
@@ -1771,32 +1779,70 @@ gemm_wgp(GemmProblem g, TileMap tm, int per_xcd)
         c0 = static_cast<int64_t>(in / rows_in_group) * BC;
     };
 
+    // Per-lane direct-load offsets, the same for every tile (all tiles are
+    // whole): computed for the tile at row 0.
     OpA opA;
     OpB opB;
-    opA.init(g.A, g.lda, 0, g.R, g.P, wr, lane, wr * TR);
-    opB.init(g.B, g.ldb, 0, g.C, g.P, wr, lane, wc * TC);
+    if constexpr (TRANS) {
+        opA.init(g.A, g.lda, 0, g.R, g.P, wr, lane, wr * TR);
+        opB.init(g.B, g.ldb, 0, g.C, g.P, wr, lane, wc * TC);
+    } else {
+        opA.init(g.A, g.lda, 0, g.R, g.P, wr, lane);
+        opB.init(g.B, g.ldb, 0, g.C, g.P, wr, lane);
+    }
     // Stage kt of the tile at (r0, c0) into (lA, lB), by the loading waves.
     auto dma = [&](uint16_t *lA, uint16_t *lB, int64_t r0, int64_t c0, int64_t kt) {
         if (!loads)
             return;
-        const __amdgpu_buffer_rsrc_t ra = tile_rsrc(g.A + kt * BK * g.lda + r0);
-        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(g.B + kt * BK * g.ldb + c0);
+        __amdgpu_buffer_rsrc_t ra, rb;
+        int soff;
+        if constexpr (TRANS) {
+            ra = tile_rsrc(g.A + kt * BK * g.lda + r0);
+            rb = tile_rsrc(g.B + kt * BK * g.ldb + c0);
+            soff = 0;
+        } else {
+            ra = tile_rsrc(g.A + r0 * g.lda);
+            rb = tile_rsrc(g.B + c0 * g.ldb);
+            soff = static_cast<int>(kt * BK * 2);
+        }
 #pragma unroll
         for (int i = 0; i < OpA::NB; ++i)
-            dma16_untracked(ra, lds_addr(lA + (wr * OpA::NB + i) * 512), opA.off[i], 0);
+            dma16_untracked(ra, lds_addr(lA + (wr * OpA::NB + i) * 512), opA.off[i], soff);
 #pragma unroll
         for (int i = 0; i < OpB::NB; ++i)
-            dma16_untracked(rb, lds_addr(lB + (wr * OpB::NB + i) * 512), opB.off[i], 0);
+            dma16_untracked(rb, lds_addr(lB + (wr * OpB::NB + i) * 512), opB.off[i], soff);
     };
 
+    // k-contiguous layout: fragment i of the wave covers tile rows
+    // wr*TR + 32i + lane%32; its chunk key depends on i only through parity.
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    const int fbA = (wr * TR + lrow) * BK;
+    const int fbB = (wc * TC + lrow) * BK;
+    int keyA[2], keyB[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        keyA[par] = khalf ^ lds_swz<BK>(wr * TR + par * 32 + lrow);
+        keyB[par] = khalf ^ lds_swz<BK>(wc * TC + par * 32 + lrow);
+    }
     bf16x8 fa[2][FR], fb[2][FC];
     auto frag_load = [&](const uint16_t *lA, const uint16_t *lB, int kk, int sl) {
 #pragma unroll
-        for (int i = 0; i < FR; ++i)
-            fa[sl][i] = opA.frag(lA, i, kk);
+        for (int i = 0; i < FR; ++i) {
+            if constexpr (TRANS)
+                fa[sl][i] = opA.frag(lA, i, kk);
+            else
+                fa[sl][i] = *reinterpret_cast<const bf16x8 *>(
+                    &lA[fbA + i * 32 * BK + (((2 * kk) ^ keyA[i & 1]) * 8)]);
+        }
 #pragma unroll
-        for (int j = 0; j < FC; ++j)
-            fb[sl][j] = opB.frag(lB, j, kk);
+        for (int j = 0; j < FC; ++j) {
+            if constexpr (TRANS)
+                fb[sl][j] = opB.frag(lB, j, kk);
+            else
+                fb[sl][j] = *reinterpret_cast<const bf16x8 *>(
+                    &lB[fbB + j * 32 * BK + (((2 * kk) ^ keyB[j & 1]) * 8)]);
+        }
     };
     f32x16 acc[FR][FC];
     auto mfma_rows = [&](int sl, int i0, int i1) {
@@ -1837,25 +1883,52 @@ gemm_wgp(GemmProblem g, TileMap tm, int per_xcd)
 #pragma unroll
             for (int i = 0; i < FR; ++i) {
                 // Lane (cl, hl) holds rows 8q + 4hl .. + 3 of output row cl.
+                if constexpr (BF) {
+                    // 32 rows of 64 bytes; 16-byte chunk q of row c at q ^ ((c >> 2) & 3).
+                    char *ob = reinterpret_cast<char *>(own);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float4 v;
-                    v.x = acc[i][t][4 * q + 0];
-                    v.y = acc[i][t][4 * q + 1];
-                    v.z = acc[i][t][4 * q + 2];
-                    v.w = acc[i][t][4 * q + 3];
-                    *reinterpret_cast<float4 *>(&own[cl * 32 + (((2 * q + hl) ^ wgp_swz(cl)) << 2)]) =
-                        v;
-                }
-                // Eight lanes per 128-byte row, eight rows per store.
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x2 lo = {acc[i][t][4 * q + 0], acc[i][t][4 * q + 1]};
+                        const f32x2 hi = {acc[i][t][4 * q + 2], acc[i][t][4 * q + 3]};
+                        uint2 w;
+                        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+                        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+                        *reinterpret_cast<uint2 *>(ob + cl * 64 + ((q ^ ((cl >> 2) & 3)) << 4) +
+                                                   hl * 8) = w;
+                    }
+                    // Four lanes per 64-byte row, sixteen rows per store.
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int rr = 8 * s + (lane >> 3), kc = lane & 7;
-                    const float4 v =
-                        *reinterpret_cast<const float4 *>(&own[rr * 32 + ((kc ^ wgp_swz(rr)) << 2)]);
-                    float *out = static_cast<float *>(g.D) + (c0 + wc * TC + t * 32 + rr) * g.ldd +
-                                 r0 + wr * TR + i * 32 + 4 * kc;
-                    store16(out, v, true);
+                    for (int s = 0; s < 2; ++s) {
+                        const int rr = 16 * s + (lane >> 2), kc = lane & 3;
+                        const uint4 v = *reinterpret_cast<const uint4 *>(
+                            ob + rr * 64 + ((kc ^ ((rr >> 2) & 3)) << 4));
+                        uint16_t *out = static_cast<uint16_t *>(g.D) +
+                                        (c0 + wc * TC + t * 32 + rr) * g.ldd + r0 + wr * TR +
+                                        i * 32 + 8 * kc;
+                        store16(out, v, true);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float4 v;
+                        v.x = acc[i][t][4 * q + 0];
+                        v.y = acc[i][t][4 * q + 1];
+                        v.z = acc[i][t][4 * q + 2];
+                        v.w = acc[i][t][4 * q + 3];
+                        *reinterpret_cast<float4 *>(
+                            &own[cl * 32 + (((2 * q + hl) ^ persist_swz(cl)) << 2)]) = v;
+                    }
+                    // Eight lanes per 128-byte row, eight rows per store.
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int rr = 8 * s + (lane >> 3), kc = lane & 7;
+                        const float4 v = *reinterpret_cast<const float4 *>(
+                            &own[rr * 32 + ((kc ^ persist_swz(rr)) << 2)]);
+                        float *out = static_cast<float *>(g.D) +
+                                     (c0 + wc * TC + t * 32 + rr) * g.ldd + r0 + wr * TR +
+                                     i * 32 + 4 * kc;
+                        store16(out, v, true);
+                    }
                 }
             }
     };
@@ -1933,9 +2006,9 @@ gemm_wgp(GemmProblem g, TileMap tm, int per_xcd)
     }
 }
 
-// gemm_wgp's shapes: whole tiles, an even number of 64-deep stages, and at
-// least two tiles per CU in whole groups of eight (one range per XCD).
-bool wgp_fits(const GemmProblem &p)
+// gemm_persist's shapes: whole tiles, an even number of 64-deep stages, and
+// at least two tiles per CU in whole groups of eight (one range per XCD).
+bool persist_fits(const GemmProblem &p)
 {
     if (p.psplit != 0 || p.R % 256 != 0 || p.C % 256 != 0 || p.P % 128 != 0 || p.P == 0)
         return false;
@@ -1943,7 +2016,8 @@ bool wgp_fits(const GemmProblem &p)
     return tiles >= 512 && tiles % kXcds == 0;
 }
 
-hipError_t launch_wgp(const GemmProblem &p, int group_r, hipStream_t s)
+template <bool TRANS>
+hipError_t launch_persist(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 {
     TileMap tm;
     tm.tiles_r = static_cast<int>(p.R / 256);
@@ -1951,7 +2025,12 @@ hipError_t launch_wgp(const GemmProblem &p, int group_r, hipStream_t s)
     tm.group_r = std::min(std::max(group_r, 1), tm.tiles_r);
     const int per_xcd = tm.tiles_r * tm.tiles_c / kXcds;
     // One workgroup per CU (160 KiB of LDS each).
-    hipLaunchKernelGGL(gemm_wgp, dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+    if (epi == Epi::kStoreF32)
+        hipLaunchKernelGGL((gemm_persist<TRANS, 0>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+    else if (epi == Epi::kStoreBF16)
+        hipLaunchKernelGGL((gemm_persist<TRANS, 1>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -2089,6 +2168,19 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
 #ifndef LMH_PP
 #define LMH_PP 1
 #endif
+    // Whole tiles (V and M multiples of 256, K of 128, at least 512 tiles):
+    // the persistent kernel, whose output stores overlap the next tile.
+    // Measured on MI355X against the routing below (bitwise-identical output,
+    // FP32 out, V=32768, three rounds of 20): M=1024 K=1024 82.6-83.3 ->
+    // 78.8-79.7 us, K=2048 131.9-135.4 -> 127.0-128.5, K=4096 239.9-241.9 ->
+    // 244.1-246.0, K=8192 479.7-485.0 -> 461.3-467.7, K=16384 929-932 ->
+    // 920-923; M=2048 K=4096 468-477 -> 457-462; M=4096 K=8192 1879-1894 ->
+    // 1849-1857; M=1024 K=8192 V=131072 1883-1899 -> 1846-1854.
+#ifndef LMH_LOGITS_PERSIST
+#define LMH_LOGITS_PERSIST 1
+#endif
+    if (LMH_LOGITS_PERSIST && (epi == Epi::kStoreF32 || epi == Epi::kStoreBF16) && persist_fits(p))
+        return launch_persist<false>(p, epi, 8, s);
     if (LMH_PP && p.P % 32 == 0 && (p.P <= 2048 || (p.C <= 384 && p.P <= 8192)) &&
         epi != Epi::kAccumF32)
         return launch_pp(p, epi, 8, s);
@@ -2136,15 +2228,15 @@ hipError_t launch_bwd(const GemmProblem &p, Epi epi, hipStream_t s)
 #endif
     if constexpr (AT && BT) {
         // Whole-tile wgrad with the store epilogue: the persistent kernel,
-        // whose dW stores overlap the next tile.  Measured on MI355X against
+        // whose dW stores overlap the next tile (gemm_persist<true>).  Measured on MI355X against
         // the kernels below (bitwise-identical dW), K=8192 V=32768: M=128
         // 197-215 -> 184-189 us, M=256 259 -> 199-208, M=512 365-369 ->
         // 304-305, M=768 485-488 -> 411-418, M=1024 573-575 -> 514-516,
         // M=4096 1784-1809 -> 1755-1770; K=16384 V=131072: M=128 1477-1594 ->
         // 1427, M=512 2918-3000 -> 2365-2373, M=4096 14217-14241 ->
         // 13687-13760 us.
-        if (epi == Epi::kStoreF32 && wgp_fits(p))
-            return launch_wgp(p, wgrad_group, s);
+        if (epi == Epi::kStoreF32 && persist_fits(p))
+            return launch_persist<true>(p, epi, wgrad_group, s);
         if (p.P <= LMH_WGRAD_WG2 && tiles256x128 >= 512)
             return launch_wg2(p, epi, wgrad_group, s);
     }

@@ -370,6 +370,32 @@ def test_wgrad_random_sampled():
     assert_gemm_close(host_f32(dw)[rows], ref, S, 1e-5, "wgrad")
 
 
+# The many-token logits GEMM over whole tiles (V, M multiples of 256, K of
+# 128, at least 512 tiles) runs the persistent kernel: the next tile's first
+# stages load while the finished tile is stored.  M=1024 K=128 (two stages
+# per tile, the least) checks every output word; M=512 K=2048 V=65536
+# (uneven tiles per workgroup: none here, 64 per XCD) sampled rows.  Padded
+# outputs pre-filled with NaN: no word missed, padding untouched.
+@pytest.mark.parametrize("M,K,V", [(1024, 128, 32768), (512, 2048, 65536)])
+def test_logits_persistent_integer_exact(M, K, V):
+    inp = workloads.integer_gemm(M, K, V, seed=8100 + K, with_targets=False)
+    _say(f"logits persistent int M={M} K={K} V={V}")
+    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    out = padded_out(M, V, V + 8, torch.float32)
+    outb = padded_out(M, V, V + 8, torch.bfloat16)
+    lmh.lmhead_logits(x, W, out=out, out_dtype="fp32")
+    lmh.lmhead_logits(x, W, out=outb, out_dtype="bf16")
+    torch.cuda.synchronize()
+    assert padding_untouched(out) and padding_untouched(outb)
+    assert not torch.isnan(out).any().item()
+    rows = None if K == 128 else np.unique(np.concatenate(
+        [np.arange(0, 40), np.arange(M - 40, M), np.random.default_rng(K).integers(0, M, 48)]))
+    L, _ = oracle.logits(inp.x, inp.W, rows=rows)
+    sel = slice(None) if rows is None else torch.from_numpy(rows).cuda()
+    assert np.array_equal(_f32_bits(host_f32(out[sel])), _f32_bits(L.astype(np.float32)))
+    assert np.array_equal(host_bits(outb[sel]), oracle.round_bf16(L))
+
+
 # wgrad over whole tiles with the store epilogue runs the persistent kernel:
 # one workgroup per CU walking its XCD's tiles, the next tile's first two
 # stages loaded while the finished tile is stored.  Cases: two stages (the
