@@ -376,11 +376,13 @@ def test_wgrad_random_sampled():
 # per tile, the least) checks every output word; M=512 K=2048 V=65536
 # (uneven tiles per workgroup: none here, 64 per XCD) sampled rows.  Padded
 # outputs pre-filled with NaN: no word missed, padding untouched.
-@pytest.mark.parametrize("M,K,V", [(1024, 128, 32768), (512, 2048, 65536)])
-def test_logits_persistent_integer_exact(M, K, V):
+@pytest.mark.parametrize("M,K,V,pad", [(1024, 128, 32768, 0), (512, 2048, 65536, 64)])
+def test_logits_persistent_integer_exact(M, K, V, pad):
+    """pad > 0: x and W inside wider NaN-filled rows (lda = ldb = K + pad),
+    which no whole tile may read."""
     inp = workloads.integer_gemm(M, K, V, seed=8100 + K, with_targets=False)
-    _say(f"logits persistent int M={M} K={K} V={V}")
-    x, W = dev_bf16(inp.x), dev_bf16(inp.W)
+    _say(f"logits persistent int M={M} K={K} V={V} pad={pad}")
+    x, W = dev_bf16(inp.x, K + pad), dev_bf16(inp.W, K + pad)
     out = padded_out(M, V, V + 8, torch.float32)
     outb = padded_out(M, V, V + 8, torch.bfloat16)
     lmh.lmhead_logits(x, W, out=out, out_dtype="fp32")
@@ -400,12 +402,13 @@ def test_logits_persistent_integer_exact(M, K, V):
 # one workgroup per CU walking its XCD's tiles, the next tile's first two
 # stages loaded while the finished tile is stored.  Cases: two stages (the
 # least, M=128), three stage pairs (M=384), uneven tiles per workgroup (520
-# tiles: 65 per XCD over 32 workgroups), a padded dW pre-filled with NaN.
-@pytest.mark.parametrize("M,K,V", [(128, 2048, 16640), (384, 4096, 8192)])
-def test_wgrad_persistent_integer_exact(M, K, V):
+# tiles: 65 per XCD over 32 workgroups), a padded dW pre-filled with NaN, and
+# operands inside wider NaN-filled rows.
+@pytest.mark.parametrize("M,K,V,pad", [(128, 2048, 16640, 0), (384, 4096, 8192, 24)])
+def test_wgrad_persistent_integer_exact(M, K, V, pad):
     dl_bits, x_bits = workloads.integer_operands([(M, V), (M, K)], seed=7000 + M)
-    _say(f"wgrad persistent int M={M} K={K} V={V}")
-    dl, x = dev_bf16(dl_bits), dev_bf16(x_bits)
+    _say(f"wgrad persistent int M={M} K={K} V={V} pad={pad}")
+    dl, x = dev_bf16(dl_bits, V + pad), dev_bf16(x_bits, K + pad)
     dw = padded_out(V, K, K + 4, torch.float32)
     lmh.lmhead_wgrad(dl, x, dW=dw)
     torch.cuda.synchronize()
