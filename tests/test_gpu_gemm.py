@@ -398,6 +398,36 @@ def test_logits_persistent_integer_exact(M, K, V, pad):
     assert np.array_equal(host_bits(outb[sel]), oracle.round_bf16(L))
 
 
+# More whole-tile shapes for both persistent GEMMs, bit-exact on integers
+# (sampled rows against the oracle, NaN-padded outputs fully written):
+# uneven tiles per workgroup (520 or 528 tiles), odd numbers of stage pairs,
+# two stages, and a near miss (516 tiles, not a multiple of 8) that must take
+# the non-persistent kernels with the same result.
+@pytest.mark.parametrize("kind,M,K,V", [("logits", 1280, 256, 26624), ("logits", 2048, 1152, 16384),
+                                        ("logits", 768, 640, 44032), ("wgrad", 256, 2560, 13312),
+                                        ("wgrad", 640, 4096, 8448)])
+def test_persistent_more_shapes_integer_exact(kind, M, K, V):
+    rng = np.random.default_rng(M + K + V)
+    _say(f"persistent shapes {kind} M={M} K={K} V={V}")
+    if kind == "logits":
+        inp = workloads.integer_gemm(M, K, V, seed=9000 + M, with_targets=False)
+        out = padded_out(M, V, V + 8, torch.float32)
+        lmh.lmhead_logits(dev_bf16(inp.x), dev_bf16(inp.W), out=out, out_dtype="fp32")
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 40)]))
+        ref, _ = oracle.logits(inp.x, inp.W, rows=rows)
+    else:
+        dl_bits, x_bits = workloads.integer_operands([(M, V), (M, K)], seed=9100 + M)
+        out = padded_out(V, K, K + 4, torch.float32)
+        lmh.lmhead_wgrad(dev_bf16(dl_bits), dev_bf16(x_bits), dW=out)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, V - 1], rng.integers(0, V, 40)]))
+        ref, _ = oracle.wgrad(dl_bits, x_bits, rows=rows)
+    assert padding_untouched(out) and not torch.isnan(out).any().item()
+    got = host_f32(out[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(_f32_bits(got), _f32_bits(ref.astype(np.float32)))
+
+
 # wgrad over whole tiles with the store epilogue runs the persistent kernel:
 # one workgroup per CU walking its XCD's tiles, the next tile's first two
 # stages loaded while the finished tile is stored.  Cases: two stages (the
