@@ -428,6 +428,42 @@ def test_persistent_more_shapes_integer_exact(kind, M, K, V):
     assert np.array_equal(_f32_bits(got), _f32_bits(ref.astype(np.float32)))
 
 
+def test_persistent_repeatable_bitwise():
+    """The persistent kernels count their direct loads and stores by hand
+    (loads untracked by the compiler): twelve launches each of the logits GEMM
+    and wgrad at M=1024 K=8192 V=32768 on random operands, interleaved with
+    other work that changes the memory system's timing (the CE on the same
+    logits, a 256 MiB fill), must all give the first launch's output bit for
+    bit."""
+    rng = np.random.default_rng(workloads.SEED + 91)
+    x_bits = workloads.normal_bf16(rng, (1024, 8192), 1.0)
+    W_bits = workloads.normal_bf16(rng, (32768, 8192), 0.02)
+    dl_bits = workloads.normal_bf16(rng, (1024, 32768), 1e-3)
+    x, W, dl = dev_bf16(x_bits), dev_bf16(W_bits), dev_bf16(dl_bits)
+    t = torch.from_numpy(rng.integers(0, 32768, 1024).astype(np.int32)).cuda()
+    _say("persistent repeatability 1024x8192x32768")
+    z0 = lmh.lmhead_logits(x, W, out_dtype="fp32")
+    w0 = lmh.lmhead_wgrad(dl, x)
+    z = torch.empty_like(z0)
+    w = torch.empty_like(w0)
+    junk = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    bad = 0
+    for i in range(12):
+        if i % 3 == 1:
+            junk.fill_(i)
+        lmh.lmhead_logits(x, W, out=z, out_dtype="fp32")
+        if i % 3 == 2:
+            lmh.lmhead_xent_fwd(z, t)
+        lmh.lmhead_wgrad(dl, x, dW=w)
+        bad += int(not torch.equal(z.view(torch.int32), z0.view(torch.int32)))
+        bad += int(not torch.equal(w.view(torch.int32), w0.view(torch.int32)))
+    torch.cuda.synchronize()
+    assert bad == 0
+    rows = np.array([0, 511, 1023])
+    ref, S = oracle.logits(x_bits, W_bits, rows=rows)
+    assert_gemm_close(host_f32(z0)[rows], ref, S, 1e-5, "logits")
+
+
 # wgrad over whole tiles with the store epilogue runs the persistent kernel:
 # one workgroup per CU walking its XCD's tiles, the next tile's first two
 # stages loaded while the finished tile is stored.  Cases: two stages (the
