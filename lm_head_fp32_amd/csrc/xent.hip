@@ -71,7 +71,7 @@ __device__ __forceinline__ float max4(const float4 &v)
     return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
 }
 
-// The single-read kernels keep each value's exponential: v <- exp(v - m_t)
+// The single-read kernel keeps each value's exponential: v <- exp(v - m_t)
 // (and the tail value when present), d += every one of them, with m_t the
 // thread's own maximum; when m_t = -inf every value is -inf and every e is 0.
 // The gradient then needs one multiply per value: exp(z - m) dloss / d =
@@ -410,14 +410,31 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(const float *z, int64_t ld
     }
 }
 
+// Four FP32 values to four BF16 (two 32-bit words), nearest-even, by the
+// hardware's paired conversion.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 bf16x4_rne(const float4 &o)
+{
+    const f32x2 lo = {o.x, o.y}, hi = {o.z, o.w};
+    uint2 w;
+    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+    return w;
+}
+
 // Fused forward + backward for a known upstream gradient: one workgroup per
 // row holds the row in registers (PER float4 per thread), so the logits are
-// read once.  The row's (m, d) come from the same per-thread pairs, wave
-// butterfly and cross-wave merge as the forward; every thread then writes
-// the gradients of exactly the elements it read (in place is safe), with the
-// backward kernel's formula.  Also writes the forward's stats record and loss.
-template <int NT, int PER, bool OUTBF16>
-__global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t ld, int64_t V,
+// read once.  Each thread reduces its values to a pair (m_t, d_t) and keeps
+// e = exp(z - m_t) in place of z; a wave butterfly and, in every wave, a
+// butterfly over the waves' pairs give all threads the row's (m, d) with one
+// barrier.  Every thread then writes the gradients of exactly the elements it
+// read (in place is safe), with the backward kernel's formula: e * scale, and
+// fmaf(e, scale, -dloss) at the target column.  Thread 0 writes the forward's
+// stats record and loss.
+template <int NT, int PER, bool WHOLE, bool OUTBF16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT * 8 / (128 * PER))))
+void xent_fused_kernel(const float *z, int64_t ld, int64_t V,
                                                         const int32_t *__restrict__ tgt,
                                                         int32_t ignore_index,
                                                         const float *__restrict__ dloss,
@@ -426,25 +443,44 @@ __global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t 
                                                         float4 *__restrict__ stats, void *g,
                                                         int64_t ldg)
 {
+    static_assert(NT % 64 == 0 && (NT / 64 & (NT / 64 - 1)) == 0 && NT / 64 <= 64, "wave count");
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     const float *zr = z + row * ld;
     const float4 *z4 = reinterpret_cast<const float4 *>(zr);
-    const int64_t n4 = V >> 2;
-    const int64_t jt = 4 * n4 + tid;  // this thread's tail column (tid < 4)
-    const bool has_tail = tid < 4 && jt < V;
+    // WHOLE: V == 4 * NT * PER, every thread holds PER whole float4 and there
+    // is no tail.  Otherwise V <= 4 * NT * PER, with a ragged last chunk and
+    // up to 3 tail columns.
+    const int n4 = WHOLE ? NT * PER : static_cast<int>(V >> 2);
+    const int jt = 4 * n4 + tid;  // this thread's tail column (tid < 4)
+    const bool has_tail = !WHOLE && tid < 4 && jt < V;
+    auto in_row = [&](int p) { return WHOLE || p * NT + tid < n4; };
 
+    // Every load is issued unconditionally (a column outside the row reads the
+    // row's first float4 and is then replaced by -inf), so that the loads stay
+    // in flight together.
     float4 v[PER];
+    const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (WHOLE || n4 > 0) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-        const int64_t i = static_cast<int64_t>(p) * NT + tid;
-        v[p] = (i < n4) ? ld4<true>(z4 + i)
-                        : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        for (int p = 0; p < PER; ++p) {
+            const bool ok = in_row(p);
+            const float4 t = ld4<true>(ok ? z4 + p * NT + tid : z4);
+            v[p] = ok ? t : ninf;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+            v[p] = ninf;
     }
     float tv = has_tail ? zr[jt] : -INFINITY;
+    const int32_t y = tgt[row];
+    const bool ignored = (y == ignore_index);
+    const bool bad = !ignored && (y < 0 || static_cast<int64_t>(y) >= V);
+    float x = 0.0f;  // the target logit, read by thread 0 before any gradient store
+    if (tid == 0 && !ignored && !bad)
+        x = zr[y];
 
-    // Per thread: m_t = its max, e = exp(z - m_t) kept in place of z, d_t =
-    // sum of e (all zero when every value is -inf).
     float m = tv;
 #pragma unroll
     for (int p = 0; p < PER; ++p)
@@ -458,76 +494,96 @@ __global__ __launch_bounds__(NT) void xent_fused_kernel(const float *z, int64_t 
         const float d2 = __shfl_xor(d, off, 64);
         merge_md(m, d, m2, d2);
     }
+    // Lane l of every wave takes wave (l mod NW)'s pair; a butterfly over NW
+    // lanes leaves every lane with the merge of all NW pairs.  merge_md is
+    // symmetric in its two pairs (max, and a sum of two products), so every
+    // lane, in every wave, holds the same bits.
     constexpr int NW = NT / 64;
-    __shared__ float sm[NW], sd[NW];
-    __shared__ float row_m, row_d;
-    if ((tid & 63) == 0) {
-        sm[tid >> 6] = m;
-        sd[tid >> 6] = d;
-    }
+    __shared__ float2 smd[NW];
+    __shared__ float sx;
+    if ((tid & 63) == 0)
+        smd[tid >> 6] = make_float2(m, d);
+    if (tid == 0)
+        sx = x;  // consumes the load of x before the barrier (in place: no store overtakes it)
     __syncthreads();
-    const int32_t y = tgt[row];
-    const bool ignored = (y == ignore_index);
-    const bool bad = !ignored && (y < 0 || static_cast<int64_t>(y) >= V);
+    {
+        const float2 q = smd[tid & (NW - 1)];
+        m = q.x;
+        d = q.y;
+#pragma unroll
+        for (int off = NW / 2; off >= 1; off >>= 1) {
+            const float m2 = __shfl_xor(m, off, 64);
+            const float d2 = __shfl_xor(d, off, 64);
+            merge_md(m, d, m2, d2);
+        }
+    }
     if (tid == 0) {
-        m = sm[0];
-        d = sd[0];
-        for (int w = 1; w < NW; ++w)
-            merge_md(m, d, sm[w], sd[w]);
-        float x, l;
+        x = sx;
+        float l;
         if (ignored) {
-            x = 0.0f;
             l = 0.0f;
         } else if (bad) {
             x = __int_as_float(0x7fc00000);
             l = x;
         } else {
-            x = zr[y];
             l = (m - x) + logf(d);
         }
         stats[row] = make_float4(m, d, x, l);
         if (loss)
             loss[row] = l;
-        row_m = m;
-        row_d = d;
     }
-    __syncthreads();
-    m = row_m;
-    d = row_d;
-    const float up = ignored ? 0.0f : dloss[dloss_stride * row];
-    // exp(z - m) / d * dloss = e * exp(m_t - m) * dloss / d
-    const float scale = grad_scale(m_t, m, d, up, bad);
 
-    auto grad = [&](float e, int64_t j) {
-        if (ignored)
-            return 0.0f;
-        return (j == static_cast<int64_t>(y)) ? fmaf(e, scale, -up) : e * scale;
+    // Chunk p of the row's gradient starts at a uniform address (p * NT
+    // float4); each thread adds only its own index.
+    auto store4 = [&](int p, const float4 &o) {
+        if constexpr (OUTBF16)
+            st2u<true>(reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g) + row * ldg) + p * NT +
+                           tid,
+                       bf16x4_rne(o));
+        else
+            st4<true>(reinterpret_cast<float4 *>(static_cast<float *>(g) + row * ldg) + p * NT + tid,
+                      o);
     };
+    auto store1 = [&](int j, float o) {
+        if constexpr (OUTBF16)
+            (static_cast<__bf16 *>(g) + row * ldg)[j] = static_cast<__bf16>(o);
+        else
+            (static_cast<float *>(g) + row * ldg)[j] = o;
+    };
+    if (ignored) {  // the whole row's gradient is zero, whatever its logits
+        const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+            if (in_row(p))
+                store4(p, zero);
+        if (has_tail)
+            store1(jt, 0.0f);
+        return;
+    }
+    const float up = dloss[dloss_stride * row];
+    // exp(z - m) / d * dloss = e * exp(m_t - m) * dloss / d (NaN for a bad target)
+    const float scale = grad_scale(m_t, m, d, up, bad);
+    const int iy = bad ? -1 : (y >> 2);  // the float4 that holds the target column
+    const int yl = y & 3;
+    if (has_tail)
+        store1(jt, (jt == y) ? fmaf(tv, scale, -up) : tv * scale);
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-        const int64_t i = static_cast<int64_t>(p) * NT + tid;
-        if (i >= n4)
+        if (!in_row(p))
             break;
-        float4 o;
-        o.x = grad(v[p].x, 4 * i);
-        o.y = grad(v[p].y, 4 * i + 1);
-        o.z = grad(v[p].z, 4 * i + 2);
-        o.w = grad(v[p].w, 4 * i + 3);
-        if constexpr (OUTBF16) {
-            uint2 w;
-            w.x = f32_to_bf16_bits(o.x) | (f32_to_bf16_bits(o.y) << 16);
-            w.y = f32_to_bf16_bits(o.z) | (f32_to_bf16_bits(o.w) << 16);
-            st2u<true>(reinterpret_cast<uint2 *>(static_cast<uint16_t *>(g) + row * ldg) + i, w);
-        } else {
-            st4<true>(reinterpret_cast<float4 *>(static_cast<float *>(g) + row * ldg) + i, o);
+        const float4 e = v[p];
+        float4 o = make_float4(e.x * scale, e.y * scale, e.z * scale, e.w * scale);
+        if (p * NT + tid == iy) {  // one thread of the row
+            if (yl == 0)
+                o.x = fmaf(e.x, scale, -up);
+            else if (yl == 1)
+                o.y = fmaf(e.y, scale, -up);
+            else if (yl == 2)
+                o.z = fmaf(e.z, scale, -up);
+            else
+                o.w = fmaf(e.w, scale, -up);
         }
-    }
-    if (has_tail) {
-        const float o = grad(tv, jt);
-        if constexpr (OUTBF16)
-            (static_cast<uint16_t *>(g) + row * ldg)[jt] = static_cast<uint16_t>(f32_to_bf16_bits(o));
-        else
-            (static_cast<float *>(g) + row * ldg)[jt] = o;
+        store4(p, o);
     }
 }
 
@@ -726,20 +782,23 @@ hipError_t launch_xent_fused(const float *logits, int64_t ld, int64_t n_rows, in
         float *l = loss ? loss + r0 : nullptr;
         float4 *st = reinterpret_cast<float4 *>(stats) + r0;
         void *g = static_cast<char *>(dlogits) + r0 * ldg * gsz;
-#define LMH_FUSED_LAUNCH(PER, BF)                                                               \
-    hipLaunchKernelGGL((xent_fused_kernel<1024, PER, BF>), grid, block, 0, s, z, ld, n_cols, t,   \
-                       ignore_index, dl, dloss_stride, l, st, g, ldg)
-        if (n_cols <= 4 * 1024 * 8) {
-            if (bf16_out)
-                LMH_FUSED_LAUNCH(8, true);
-            else
-                LMH_FUSED_LAUNCH(8, false);
-        } else {
-            if (bf16_out)
-                LMH_FUSED_LAUNCH(16, true);
-            else
-                LMH_FUSED_LAUNCH(16, false);
-        }
+#define LMH_FUSED_LAUNCH(PER, WHOLE)                                                            \
+    do {                                                                                        \
+        if (bf16_out)                                                                           \
+            hipLaunchKernelGGL((xent_fused_kernel<1024, PER, WHOLE, true>), grid, block, 0, s, z, \
+                               ld, n_cols, t, ignore_index, dl, dloss_stride, l, st, g, ldg);   \
+        else                                                                                    \
+            hipLaunchKernelGGL((xent_fused_kernel<1024, PER, WHOLE, false>), grid, block, 0, s,   \
+                               z, ld, n_cols, t, ignore_index, dl, dloss_stride, l, st, g, ldg); \
+    } while (0)
+        if (n_cols == 4 * 1024 * 8)
+            LMH_FUSED_LAUNCH(8, true);
+        else if (n_cols < 4 * 1024 * 8)
+            LMH_FUSED_LAUNCH(8, false);
+        else if (n_cols == 4 * 1024 * 16)
+            LMH_FUSED_LAUNCH(16, true);
+        else
+            LMH_FUSED_LAUNCH(16, false);
 #undef LMH_FUSED_LAUNCH
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)

@@ -198,16 +198,20 @@ def test_target_lane_every_residue():
     dl_host = rng.uniform(0.25, 2.0, n).astype(np.float32)
     _say(f"target lanes n={n} V={V}")
     z, t = dev_f32(logits, (V + 3) // 4 * 4), dev_i32(tgt)
+    dl = torch.from_numpy(dl_host).cuda()
     _, st = lmh.lmhead_xent_fwd(z, t)
-    g = lmh.lmhead_xent_bwd(z, st, t, torch.from_numpy(dl_host).cuda())
-    gb = lmh.lmhead_xent_bwd(z, st, t, torch.from_numpy(dl_host).cuda(), grad_dtype="bf16")
+    g = lmh.lmhead_xent_bwd(z, st, t, dl)
+    gb = lmh.lmhead_xent_bwd(z, st, t, dl, grad_dtype="bf16")
+    _, _, gf = lmh.lmhead_xent_fused(z, t, dl)                       # one-read kernel
+    _, _, gfb = lmh.lmhead_xent_fused(z, t, dl, grad_dtype="bf16")
     torch.cuda.synchronize()
-    gh = host_f32(g)
-    neg = [np.flatnonzero(gh[r] < 0).tolist() for r in range(n)]
-    assert neg == [[int(y)] for y in tgt]
     g_ref = oracle.xent_bwd(logits, tgt, -100, dl_host.astype(np.float64))
-    _check_grad(gh, g_ref)
-    assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16))
+    for name, gg, gg16 in (("bwd", g, gb), ("fused", gf, gfb)):
+        gh = host_f32(gg)
+        neg = [np.flatnonzero(gh[r] < 0).tolist() for r in range(n)]
+        assert neg == [[int(y)] for y in tgt], name
+        _check_grad(gh, g_ref, what=name)
+        assert torch.equal(gg16.view(torch.int16), gg.to(torch.bfloat16).view(torch.int16)), name
 
 
 def test_all_rows_ignored_and_bad_target():
@@ -410,12 +414,42 @@ def test_fully_masked_row():
     z_h[1] = -np.inf
     t_h = np.array([7, -100, 7], dtype=np.int32)
     loss, st = lmh.lmhead_xent_fwd(dev_f32(z_h), dev_i32(t_h))
+    _, sf, gf = lmh.lmhead_xent_fused(dev_f32(z_h), dev_i32(t_h), torch.ones(1, device="cuda"))
     torch.cuda.synchronize()
-    sh, ref = host_f32(st), oracle.xent_fwd(z_h, t_h, -100)
-    assert np.all(sh[:2, 0] == -np.inf) and np.all(sh[:2, 1] == 0.0)
-    assert np.isnan(sh[0, 3]) and np.isnan(ref[0, 3])
-    assert sh[1, 3] == 0.0 and ref[1, 3] == 0.0
-    _check_stats(sh[2:], ref[2:], "unmasked row")
+    ref = oracle.xent_fwd(z_h, t_h, -100)
+    for name, sh in (("fwd", host_f32(st)), ("fused", host_f32(sf))):
+        assert np.all(sh[:2, 0] == -np.inf) and np.all(sh[:2, 1] == 0.0), name
+        assert np.isnan(sh[0, 3]) and np.isnan(ref[0, 3]), name
+        assert sh[1, 3] == 0.0 and ref[1, 3] == 0.0, name
+        _check_stats(sh[2:], ref[2:], name + " unmasked row")
+    gh = host_f32(gf)
+    assert np.all(gh[1] == 0.0)                      # ignored: zero gradient
+    _check_grad(gh[2:], oracle.xent_bwd(z_h[2:], t_h[2:], -100, 1.0), what="fused unmasked row")
+
+
+def test_bf16_grads_of_subnormal_size_round_like_torch():
+    """Gradients far below the row maximum (exp(z - m) down to FP32's
+    subnormal range and to zero): the BF16 gradients of the backward and the
+    fused kernel equal torch's nearest-even rounding of the same kernels'
+    FP32 gradients bit for bit, subnormals included."""
+    V = 4096 + 8
+    rng = np.random.default_rng(777)
+    z_h = rng.uniform(-110.0, 0.0, (6, V)).astype(np.float32)   # e = exp(z - m) from 1 down to 0
+    z_h[:, 5] = 0.0
+    t_h = np.array([5, 17, V - 1, 0, 4096, 3], dtype=np.int32)
+    z, t = dev_f32(z_h), dev_i32(t_h)
+    dl = torch.full((1,), 1.0, device="cuda")
+    _, st = lmh.lmhead_xent_fwd(z, t)
+    out = {}
+    out["bwd"] = (lmh.lmhead_xent_bwd(z, st, t, dl), lmh.lmhead_xent_bwd(z, st, t, dl, grad_dtype="bf16"))
+    out["fused"] = (lmh.lmhead_xent_fused(z, t, dl)[2],
+                    lmh.lmhead_xent_fused(z, t, dl, grad_dtype="bf16")[2])
+    torch.cuda.synchronize()
+    for name, (g, gb) in out.items():
+        gh = host_f32(g)
+        sub = (gh != 0) & (np.abs(gh) < np.finfo(np.float32).tiny)
+        assert sub.sum() > 100, name                     # the case is exercised
+        assert torch.equal(gb.view(torch.int16), g.to(torch.bfloat16).view(torch.int16)), name
 
 
 # ------------------------------------ calls longer than one launch can hold
