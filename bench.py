@@ -66,11 +66,11 @@ PEAK_HBM_GBS = 8000.0
 # (code hash of the .hip file, see source_code_hash).  Changed code reports null.
 MEASURED_TRAFFIC = {
     "logits_fp32": {"src": "gemm.hip", "sha": "a6e02da37c7d3a73",
-                    "bytes": int((2 * 393354.6 + 131100.5) * 1024)},
-    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "ea1a23b513ff0282",
-                          "bytes": int((2 * 2097959.4 + 513.5 + 2 * 2056473.4 + 4195416.0) * 1024)},
-    "xent_fused_bf16_1024x32768": {"src": "xent.hip", "sha": "ea1a23b513ff0282",
-                                   "bytes": int((2 * 65695.6 + 65604.5) * 1024)},
+                    "bytes": int((2 * 393346.9 + 131097.9) * 1024)},
+    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "f9dd9ac180f52b71",
+                          "bytes": int((2 * 2097959.0 + 513.8 + 2 * 2056475.7 + 4195460.9) * 1024)},
+    "xent_fused_bf16_1024x32768": {"src": "xent.hip", "sha": "f9dd9ac180f52b71",
+                                   "bytes": int((2 * 65665.7 + 65649.8) * 1024)},
 }
 
 
