@@ -181,19 +181,21 @@ def test_edge_shapes_random(n, V, dloss_mode):
     assert np.all(rs <= 1e-5 * scale + 1e-7)
 
 
-def test_target_lane_every_residue():
+@pytest.mark.parametrize("V", [9 * 1024 + 3, 32768, 40001, 65536])
+def test_target_lane_every_residue(V):
     """The one-hot term lands on the target column whatever its position in
     its 16-byte group (target mod 4 = 0..3), in the first, middle and last
-    block of a row and in the ragged tail.  With dloss > 0 the target column
-    is the only negative entry of its gradient row (softmax minus one-hot,
-    scaled), so its position is checked exactly, then every value against
-    the oracle."""
-    V = 9 * 1024 + 3
+    block of a row and in the ragged tail, for the backward and for the
+    one-read kernel's forms (8 and 16 float4 per thread, whole rows and ragged
+    ones).  With dloss > 0 the target column is the only negative entry of its
+    gradient row (softmax minus one-hot, scaled), so its position is checked
+    exactly, then every value against the oracle."""
+    mid = (V // 2) & ~3
     cols = [0, 1, 2, 3, 1020, 1021, 1022, 1023, 4100, 4101, 4102, 4103,
-            V - 7, V - 6, V - 5, V - 4, V - 3, V - 2, V - 1]
+            mid, mid + 1, mid + 2, mid + 3, V - 7, V - 6, V - 5, V - 4, V - 3, V - 2, V - 1]
     n = len(cols) * 2
     tgt = np.array(cols + cols, dtype=np.int32)
-    rng = np.random.default_rng(4242)
+    rng = np.random.default_rng(4242 + V)
     logits = rng.normal(0.0, 1.5, (n, V)).astype(np.float32)
     dl_host = rng.uniform(0.25, 2.0, n).astype(np.float32)
     _say(f"target lanes n={n} V={V}")
