@@ -434,14 +434,9 @@ __device__ __forceinline__ uint2 bf16x4_rne(const float4 &o)
 // stats record and loss.
 template <int NT, int PER, bool WHOLE, bool OUTBF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT * 8 / (128 * PER))))
-void xent_fused_kernel(const float *z, int64_t ld, int64_t V,
-                                                        const int32_t *__restrict__ tgt,
-                                                        int32_t ignore_index,
-                                                        const float *__restrict__ dloss,
-                                                        int64_t dloss_stride,
-                                                        float *__restrict__ loss,
-                                                        float4 *__restrict__ stats, void *g,
-                                                        int64_t ldg)
+void xent_fused_kernel(const float *z, int64_t ld, int64_t V, const int32_t *__restrict__ tgt,
+                       int32_t ignore_index, const float *__restrict__ dloss, int64_t dloss_stride,
+                       float *__restrict__ loss, float4 *__restrict__ stats, void *g, int64_t ldg)
 {
     static_assert(NT % 64 == 0 && (NT / 64 & (NT / 64 - 1)) == 0 && NT / 64 <= 64, "wave count");
     const int64_t row = blockIdx.x;
