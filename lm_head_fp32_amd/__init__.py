@@ -21,10 +21,11 @@ import os
 import torch
 
 __all__ = [
-    "LMH_BF16", "LMH_FP32", "LMH_FP16", "STATS_COLS", "LmheadError", "lib", "library_path",
-    "lmhead_logits", "lmhead_xent_fwd", "lmhead_xent_mean", "lmhead_xent_bwd",
-    "lmhead_dgrad", "lmhead_wgrad", "lmhead_status_str", "lmhead_version",
-    "lmhead_diag_mfma_loop", "lmhead_dgrad_workspace_bytes",
+    "LMH_BF16", "LMH_FP32", "LMH_FP16", "STATS_COLS", "DGRAD_NOALLOC_MAX_BYTES", "LmheadError",
+    "lib", "library_path", "lmhead_logits", "lmhead_logits_xent", "lmhead_xent_fwd",
+    "lmhead_xent_partial", "lmhead_xent_merge", "lmhead_xent_mean", "lmhead_xent_bwd",
+    "lmhead_xent_fused", "lmhead_dgrad", "lmhead_dgrad_noalloc", "lmhead_wgrad",
+    "lmhead_status_str", "lmhead_version", "lmhead_diag_mfma_loop", "lmhead_dgrad_workspace_bytes",
 ]
 
 LMH_BF16, LMH_FP32, LMH_FP16 = 0, 1, 2

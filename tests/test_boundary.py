@@ -41,6 +41,16 @@ def test_header_and_binding_agree():
     assert _declared_symbols() == sorted(lmh._SIGNATURES)
 
 
+def test_python_functions_carry_the_c_names():
+    """Each C entry point that computes has a Python function of the same
+    name, exported by the package (the dgrad workspace form is reached
+    through lmhead_dgrad's `workspace` argument)."""
+    wrapped = set(_declared_symbols()) - {"lmhead_dgrad_ws"}
+    for name in wrapped:
+        assert callable(getattr(lmh, name, None)), name
+        assert name in lmh.__all__, name
+
+
 def test_library_exports_every_declared_symbol(L):
     for name in _declared_symbols():
         assert hasattr(L, name), name
