@@ -2,9 +2,10 @@
 and BF16 epilogues), dgrad and wgrad on integer operands in [-8, 8], which
 are exact in FP32 at these sizes (every product and partial sum is an integer
 below 2^24), so each output must equal the FP64 oracle bit for bit; and the
-CE forward and backward on those exact logits scaled by 1/64 (a power of two,
-so still exact), with 10 % of rows ignored, against the oracle to the usual
-tolerances (m and X_y bit-exact, loss 1e-5 relative, gradient 1e-6 absolute).
+CE forward and backward, and the single-read forward + backward, on those
+exact logits scaled by 1/64 (a power of two, so still exact), with 10 % of
+rows ignored, against the oracle to the usual tolerances (m and X_y
+bit-exact, loss 1e-5 relative, gradient 1e-6 absolute).
 
 Shapes mix single rows, ragged tile edges (M, V not multiples of the tiles,
 K any multiple of 8) and padded leading dimensions, so the kernels' edge
@@ -73,3 +74,17 @@ def test_random_shape_parity(case):
     assert_loss_close(host_f32(loss), ref[:, 3])
     gref = oracle.xent_bwd(zz, t, -100, 0.25)
     assert np.max(np.abs(host_f32(grad).astype(np.float64) - gref), initial=0.0) <= 1e-6
+
+    # the single-read kernel on the same logits: FP32 and BF16 gradients
+    dl = torch.full((1,), 0.25, device="cuda")
+    floss, fst, fg = lmh.lmhead_xent_fused(zd, td, dl)
+    _, fst16, fg16 = lmh.lmhead_xent_fused(zd, td, dl, grad_dtype="bf16")
+    torch.cuda.synchronize()
+    fs = host_f32(fst).astype(np.float64)
+    assert np.array_equal(fs[:, 0], ref[:, 0])
+    assert np.array_equal(fs[:, 2], ref[:, 2])
+    assert_loss_close(fs[:, 3], ref[:, 3])
+    assert_loss_close(host_f32(floss), ref[:, 3])
+    assert torch.equal(fst.view(torch.int32), fst16.view(torch.int32))
+    assert np.max(np.abs(host_f32(fg).astype(np.float64) - gref), initial=0.0) <= 1e-6
+    assert torch.equal(fg16.view(torch.int16), fg.to(torch.bfloat16).view(torch.int16))
