@@ -410,6 +410,11 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(const float *z, int64_t ld
     }
 }
 
+// Four -inf values: what the single-read kernel loads for columns past a
+// row's end (never written).
+__device__ __attribute__((aligned(16))) float kNegInf4[4] = {-INFINITY, -INFINITY, -INFINITY,
+                                                            -INFINITY};
+
 // Four FP32 values to four BF16 (two 32-bit words), nearest-even, by the
 // hardware's paired conversion.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -451,23 +456,15 @@ void xent_fused_kernel(const float *z, int64_t ld, int64_t V, const int32_t *__r
     const bool has_tail = !WHOLE && tid < 4 && jt < V;
     auto in_row = [&](int p) { return WHOLE || p * NT + tid < n4; };
 
-    // Every load is issued unconditionally (a column outside the row reads the
-    // row's first float4 and is then replaced by -inf), so that the loads stay
-    // in flight together.
+    // Every load is issued unconditionally, so that the loads stay in flight
+    // together: a float4 past the row's end is read from a constant group of
+    // four -inf instead (no select on the loaded values, which would make each
+    // load wait before the next is issued).
     float4 v[PER];
-    const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (WHOLE || n4 > 0) {
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const bool ok = in_row(p);
-            const float4 t = ld4<true>(ok ? z4 + p * NT + tid : z4);
-            v[p] = ok ? t : ninf;
-        }
-    } else {
-#pragma unroll
-        for (int p = 0; p < PER; ++p)
-            v[p] = ninf;
-    }
+    for (int p = 0; p < PER; ++p)
+        v[p] = ld4<true>(in_row(p) ? z4 + p * NT + tid
+                                   : reinterpret_cast<const float4 *>(kNegInf4));
     float tv = has_tail ? zr[jt] : -INFINITY;
     const int32_t y = tgt[row];
     const bool ignored = (y == ignore_index);
