@@ -66,11 +66,11 @@ PEAK_HBM_GBS = 8000.0
 # (code hash of the .hip file, see source_code_hash).  Changed code reports null.
 MEASURED_TRAFFIC = {
     "logits_fp32": {"src": "gemm.hip", "sha": "a6e02da37c7d3a73",
-                    "bytes": int((2 * 393340.1 + 131081.1) * 1024)},
-    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "f9dd9ac180f52b71",
-                          "bytes": int((2 * 2097959.7 + 513.5 + 2 * 2056475.8 + 4195508.3) * 1024)},
-    "xent_fused_bf16_1024x32768": {"src": "xent.hip", "sha": "f9dd9ac180f52b71",
-                                   "bytes": int((2 * 65665.7 + 65647.7) * 1024)},
+                    "bytes": int((2 * 393352.6 + 131082.0) * 1024)},
+    "xent_fwd_bwd_fp32": {"src": "xent.hip", "sha": "94784a1df1d6afbd",
+                          "bytes": int((2 * 2097959.1 + 514.2 + 2 * 2056475.9 + 4195208.8) * 1024)},
+    "xent_fused_bf16_1024x32768": {"src": "xent.hip", "sha": "94784a1df1d6afbd",
+                                   "bytes": int((2 * 65665.8 + 65661.1) * 1024)},
 }
 
 
