@@ -434,8 +434,8 @@ def step_full(torch, lmh, steps, seed, M, K, V, w_sigma, ignore_frac):
 
 def host_cpu_share():
     """Threads the oracle may use here: the CPUs this process may run on,
-    capped by OMP_NUM_THREADS when set (the GPU machine sets it to its CPU share
-    per GPU)."""
+    capped by OMP_NUM_THREADS when set (a host shared by several GPUs sets it
+    to each GPU's CPU share)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     cap = os.environ.get("OMP_NUM_THREADS", "")
     if cap.isdigit() and int(cap) > 0:
