@@ -78,3 +78,18 @@ def test_traffic_figures_come_from_the_committed_profile():
             "xent_fused_bf16_1024x32768": "xent_fused_kernel"}
     for key, kname in want.items():
         assert abs(bench.MEASURED_TRAFFIC[key]["bytes"] - table[kname]) <= 1, key
+
+
+def test_profiles_name_the_current_kernel_sources():
+    """Each rocprofv3 summary under profiles/ states the source hash of the
+    kernels it measured; those are the sources in the tree (a kernel changed
+    since its profile was taken would make the summary describe other code)."""
+    pdir = os.path.join(ROOT, "profiles")
+    seen = 0
+    for fn in sorted(os.listdir(pdir)):
+        with open(os.path.join(pdir, fn)) as f:
+            text = f.read()
+        for name, sha in re.findall(r"(\w+\.hip) ([0-9a-f]{16})", text):
+            assert bench.source_code_hash(name) == sha, (fn, name)
+            seen += 1
+    assert seen >= 3
