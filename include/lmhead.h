@@ -30,8 +30,10 @@
  *    reports a failed launch.  Results are ready when the stream reaches
  *    that point.
  *  - Alignment: every pointer 16-byte aligned; `ld` a multiple of 8 for BF16
- *    and of 4 for FP32 (LMH_ERR_ALIGN).  ld must be >= the row length
- *    (LMH_ERR_SHAPE).  Sizes are >= 0; a zero-size output is a no-op.
+ *    and of 4 for FP32 (LMH_ERR_ALIGN).  ld must be >= the row length, and
+ *    a matrix may span at most 2^44 elements ((rows - 1) * ld + row length;
+ *    the same for a stride between blocks of records) (LMH_ERR_SHAPE).  Sizes
+ *    are >= 0; a zero-size output is a no-op.
  *    The GEMMs run fastest with 128-byte aligned rows (BF16 ld a multiple
  *    of 64); rows only 16-byte aligned are accepted but measured up to a
  *    third slower.

@@ -71,7 +71,24 @@ bool aligned4(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
 }
 
-// Byte range [lo, hi) touched by a row-major [rows x cols] matrix.
+// Elements a row-major [rows x cols] matrix with leading dimension ld may
+// span: 2^44, far beyond any GPU's memory, so that spans and kernel offsets
+// (row * ld, in 64 bits) cannot overflow.
+constexpr int64_t kMaxSpanElems = int64_t{1} << 44;
+
+// True when (rows - 1) * ld + cols stays within kMaxSpanElems (rows, cols and
+// ld non-negative; computed without overflow).
+bool span_fits(int64_t rows, int64_t cols, int64_t ld)
+{
+    if (rows <= 0 || cols <= 0)
+        return true;
+    if (ld > kMaxSpanElems || cols > kMaxSpanElems)
+        return false;
+    return rows == 1 || ld <= (kMaxSpanElems - cols) / (rows - 1);
+}
+
+// Byte range [lo, hi) touched by a row-major [rows x cols] matrix (its span
+// checked with span_fits first).
 struct Span {
     uintptr_t lo, hi;
 };
@@ -105,7 +122,7 @@ int32_t check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld, int 
         return LMH_OK;
     if (!p)
         return LMH_ERR_NULL;
-    if (ld < cols)
+    if (ld < cols || !span_fits(rows, cols, ld))
         return LMH_ERR_SHAPE;
     if (!aligned16(p) || (ld % ld_multiple) != 0)
         return LMH_ERR_ALIGN;
@@ -259,7 +276,7 @@ int32_t lmhead_logits_xent(const void *x, int64_t ldx, const void *W, int64_t ld
     if (M == 0 || V == 0)
         return LMH_OK;
     const int64_t nparts = (V + kLogitsStatsBlock - 1) / kLogitsStatsBlock;
-    if (part_stride < 4 * M)
+    if (part_stride < 4 * M || !span_fits(nparts, 4 * M, part_stride))
         return LMH_ERR_SHAPE;
     if (!target || !part)
         return LMH_ERR_NULL;
@@ -343,7 +360,7 @@ int32_t lmhead_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int
         return LMH_ERR_SHAPE;
     LMH_TRY(check_matrix(logits, n_rows, n_cols, ld, 4));
     const int64_t nb = (n_cols + block_cols - 1) / block_cols;
-    if (nb > kMaxDim / n_rows || part_stride < 4 * n_rows)
+    if (nb > kMaxDim / n_rows || part_stride < 4 * n_rows || !span_fits(nb, 4 * n_rows, part_stride))
         return LMH_ERR_SHAPE;
     if (!target || !part)
         return LMH_ERR_NULL;
@@ -366,7 +383,8 @@ int32_t lmhead_xent_merge(const float *part, int64_t n_parts, int64_t part_strid
         return LMH_ERR_SHAPE;
     if (n_rows == 0)
         return LMH_OK;
-    if (n_parts < 1 || vocab < 1 || part_stride < 4 * n_rows)
+    if (n_parts < 1 || vocab < 1 || part_stride < 4 * n_rows ||
+        !span_fits(n_parts, 4 * n_rows, part_stride))
         return LMH_ERR_SHAPE;
     if (!part || !target || !stats)
         return LMH_ERR_NULL;

@@ -385,3 +385,24 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU only" in res.stdout
+
+
+def test_spans_past_2_44_elements_are_refused(L):
+    """A leading dimension or record stride so large that the matrix would
+    span more than 2^44 elements is refused on the host (LMH_ERR_SHAPE), so
+    no span or kernel offset computed from it can overflow 64 bits."""
+    big = 1 << 62
+    f = L.lmhead_logits
+    assert f(A, 64, B, 64, C, big, FP32, 16, 64, 128, None) == SHAPE          # ldo
+    assert f(A, big, B, 64, C, 128, FP32, 16, 64, 128, None) == SHAPE         # ldx
+    assert f(A, 64, B, (1 << 44) - 8, C, 128, FP32, 16, 64, 128, None) == SHAPE  # V rows of W
+    assert f(A, 64, B, 64, C, (1 << 44) + 4, FP32, 1, 64, 128, None) == SHAPE  # ld alone too large
+    g = L.lmhead_xent_fwd
+    assert g(A, big, 4, 1024, B, -100, C, D, None) == SHAPE
+    assert g(A, 1 << 43, 3, 1024, B, -100, C, D, None) == SHAPE                # 2 x 2^43 + 1024
+    p = L.lmhead_xent_partial
+    assert p(A, 1024, 8, 1024, 0, 256, B, -100, C, big, None) == SHAPE
+    m = L.lmhead_xent_merge
+    assert m(A, 4, big, 8, B, -100, 1000, C, D, None) == SHAPE
+    x = L.lmhead_logits_xent
+    assert x(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, E, big, None) == SHAPE
