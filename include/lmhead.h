@@ -160,9 +160,9 @@ int32_t lmhead_xent_fwd(const float *logits, int64_t ld, int64_t n_rows, int64_t
  *
  *  logits  FP32 [n_rows x n_cols], leading dimension ld; the slice holds the
  *          global columns [col0, col0 + n_cols).  Read once.
- *  block_cols  columns per block, a positive multiple of 4; the slice is cut
- *          into n_blocks = ceil(n_cols / block_cols) blocks (the last one may
- *          be shorter).  n_blocks * n_rows must not exceed INT32_MAX
+ *  block_cols  columns per block, a positive multiple of 4, at most
+ *          INT32_MAX; the slice is cut into n_blocks = ceil(n_cols /
+ *          block_cols) blocks (the last one may be shorter).  n_blocks * n_rows must not exceed INT32_MAX
  *          (LMH_ERR_SHAPE).
  *  target  int32 [n_rows], GLOBAL column indices; ignore_index as in the
  *          forward.

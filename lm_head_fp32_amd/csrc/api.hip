@@ -356,7 +356,8 @@ int32_t lmhead_xent_partial(const float *logits, int64_t ld, int64_t n_rows, int
         return LMH_ERR_SHAPE;
     if (n_rows == 0)
         return LMH_OK;
-    if (n_cols < 1 || col0 < 0 || col0 > kMaxDim || block_cols < 4 || block_cols % 4 != 0)
+    if (n_cols < 1 || col0 < 0 || col0 > kMaxDim || block_cols < 4 || block_cols > kMaxDim ||
+        block_cols % 4 != 0)
         return LMH_ERR_SHAPE;
     LMH_TRY(check_matrix(logits, n_rows, n_cols, ld, 4));
     const int64_t nb = (n_cols + block_cols - 1) / block_cols;

@@ -402,6 +402,7 @@ def test_spans_past_2_44_elements_are_refused(L):
     assert g(A, 1 << 43, 3, 1024, B, -100, C, D, None) == SHAPE                # 2 x 2^43 + 1024
     p = L.lmhead_xent_partial
     assert p(A, 1024, 8, 1024, 0, 256, B, -100, C, big, None) == SHAPE
+    assert p(A, 1024, 8, 1024, 0, (1 << 63) - 4, B, -100, C, 32, None) == SHAPE   # block_cols
     m = L.lmhead_xent_merge
     assert m(A, 4, big, 8, B, -100, 1000, C, D, None) == SHAPE
     x = L.lmhead_logits_xent
