@@ -40,6 +40,15 @@ COMMON_FLAGS = [
 ]
 
 
+# A second library for CPU tests of the C ABI's argument checks: api.hip's
+# host code built with AddressSanitizer and UndefinedBehaviorSanitizer (the
+# size arithmetic of every entry point runs there), linked with the normal
+# objects of the other sources.  Never loaded by GPU runs.
+HOSTSAN_LIB = os.path.join(HERE, "liblmhead_hostsan.so")
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -77,5 +86,43 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(verbose: bool = False) -> str:
+    """liblmhead_hostsan.so (see HOSTSAN_FLAGS); needs build()'s objects."""
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: {missing} missing")
+    obj = os.path.join(BUILD_DIR, "api_hostsan.o")
+    cmd = [hipcc(), *COMMON_FLAGS, *HOSTSAN_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+           os.path.join(CSRC, "api.hip"), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on api.hip (sanitized host code):\n{res.stderr}")
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+            *HOSTSAN_FLAGS[:4], obj, *objs, "-o", HOSTSAN_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized host code):\n{res.stderr}")
+    os.replace(HOSTSAN_LIB + ".tmp", HOSTSAN_LIB)
+    return HOSTSAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """The ASan runtime (it carries the UBSan handlers) that a process loading
+    liblmhead_hostsan.so must preload; '' when not found."""
+    import glob
+
+    found = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib",
+                                          "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    return found[-1] if found else ""
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
