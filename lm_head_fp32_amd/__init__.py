@@ -144,10 +144,19 @@ def _stream(stream):
     return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _on_current_device(t, name):
+    """The kernels run on the current device (HIP launches target it), so a
+    tensor on another GPU is refused rather than read from the wrong one."""
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
 def _mat(t, name, dtype):
     """(pointer, ld) of a 2-D GPU tensor with a contiguous last dimension."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name}: expected a GPU tensor")
+    _on_current_device(t, name)
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if t.dim() != 2:
@@ -161,6 +170,7 @@ def _mat(t, name, dtype):
 def _vec(t, name, dtype, n):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name}: expected a GPU tensor")
+    _on_current_device(t, name)
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if t.numel() != n or (n > 1 and not t.is_contiguous()):
@@ -293,6 +303,7 @@ def _parts(part, n):
     """(pointer, stride between parts in elements) of an FP32 [P, n, 4] tensor."""
     if not isinstance(part, torch.Tensor) or not part.is_cuda or part.dtype != torch.float32:
         raise TypeError("part: expected a GPU float32 tensor")
+    _on_current_device(part, "part")
     if part.dim() != 3 or part.shape[1] != n or part.shape[2] != STATS_COLS:
         raise ValueError(f"part: expected shape [n_parts, {n}, {STATS_COLS}]")
     if n > 0 and (part.stride(2) != 1 or part.stride(1) != STATS_COLS):
@@ -340,6 +351,7 @@ def lmhead_xent_bwd(logits, stats, target, dloss, ignore_index=-100, dlogits=Non
     pt = _vec(target, "target", torch.int32, n)
     if not isinstance(dloss, torch.Tensor) or not dloss.is_cuda or dloss.dtype != torch.float32:
         raise TypeError("dloss: expected a GPU fp32 tensor")
+    _on_current_device(dloss, "dloss")
     if dloss.numel() == 1:
         stride = 0
     elif dloss.numel() == n and dloss.is_contiguous():
@@ -373,6 +385,7 @@ def lmhead_xent_fused(logits, target, dloss, ignore_index=-100, dlogits=None, gr
     pt = _vec(target, "target", torch.int32, n)
     if not isinstance(dloss, torch.Tensor) or not dloss.is_cuda or dloss.dtype != torch.float32:
         raise TypeError("dloss: expected a GPU fp32 tensor")
+    _on_current_device(dloss, "dloss")
     if dloss.numel() == 1:
         stride = 0
     elif dloss.numel() == n and dloss.is_contiguous():
@@ -448,6 +461,7 @@ def lmhead_dgrad(dlogits, W, dX=None, dx_dtype=None, splits=0, workspace=None, s
             workspace.record_stream(stream)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor")
+    _on_current_device(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
     _check("lmhead_dgrad_ws", lib().lmhead_dgrad_ws(pd, ldd, pw, ldw, px, ldx, code, M, K, V, splits,
                                                     workspace.data_ptr(), nbytes,
@@ -509,6 +523,9 @@ def lmhead_diag_mfma_loop(iters, n_workgroups, sink=None, stream=None, operands=
         raise ValueError("operands must be 'ones' or 'random'")
     if sink is None:
         sink = torch.empty(max(n_workgroups, 0) * 256, dtype=torch.float32, device="cuda")
+    if not isinstance(sink, torch.Tensor) or not sink.is_cuda:
+        raise TypeError("sink: expected a GPU tensor")
+    _on_current_device(sink, "sink")
     if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < n_workgroups * 256:
         raise ValueError("sink must be a contiguous fp32 tensor of n_workgroups * 256 elements")
     _check("lmhead_diag_mfma_loop",

@@ -341,10 +341,14 @@ def test_diag_mfma_loop_validation(L):
 
 
 def test_binding_rejects_cpu_tensors():
+    """Host tensors never reach a kernel: every tensor argument, outputs and
+    the diagnostic's sink included, must be a GPU tensor."""
     import torch
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         lmh.lmhead_logits(x, x)
+    with pytest.raises(TypeError):
+        lmh.lmhead_diag_mfma_loop(4, 1, sink=torch.zeros(256))
 
 
 def test_binding_output_dtype_follows_the_tensor():
@@ -407,3 +411,11 @@ def test_spans_past_2_44_elements_are_refused(L):
     assert m(A, 4, big, 8, B, -100, 1000, C, D, None) == SHAPE
     x = L.lmhead_logits_xent
     assert x(A, 64, B, 64, C, 1024, 300, 64, 1024, D, -100, E, big, None) == SHAPE
+
+    # the dgrad workspace size for an output past 2^44 elements is refused, not overflowed
+    huge = (1 << 31) - 1
+    assert L.lmhead_dgrad_workspace_bytes(huge, huge, 1024, 2) == -SHAPE
+    assert L.lmhead_dgrad_ws(A, 1024, B, huge, C, huge, FP32, huge, huge, 1024, 2, E, 1 << 40,
+                             None) == SHAPE
+    assert L.lmhead_dgrad_noalloc(A, 1024, B, huge, C, huge, FP32, huge, huge, 1024, 2,
+                                  None) == SHAPE
