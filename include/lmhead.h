@@ -316,7 +316,8 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
  *  lmhead_dgrad_workspace_bytes returns the workspace bytes that
  *  lmhead_dgrad_ws needs for (M, K, V, splits): parts x M x K4 x 4 with K4 =
  *  K rounded up to a multiple of 4, or 0 when the shape runs unsplit; a
- *  negative LMH_ERR_SHAPE for negative sizes or splits outside [0, 16].
+ *  negative LMH_ERR_SHAPE for negative sizes, splits outside [0, 16], or a dX
+ *  of more than 2^44 elements.
  *
  *  lmhead_dgrad_ws takes lmhead_dgrad's arguments plus splits and the
  *  caller's device workspace (16-byte aligned, workspace_bytes >= the size

@@ -547,8 +547,9 @@ int32_t lmhead_dgrad(const void *dlogits, int64_t ldd, const void *W, int64_t ld
 
 int64_t lmhead_dgrad_workspace_bytes(int64_t M, int64_t K, int64_t V, int32_t splits)
 {
+    // dX [M x K] must fit a matrix's span, which also keeps the size below in range.
     if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim || splits < 0 ||
-        splits > kMaxSplits)
+        splits > kMaxSplits || !span_fits(M, K + 3, K + 3))
         return -static_cast<int64_t>(LMH_ERR_SHAPE);
     return 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
 }
@@ -559,7 +560,7 @@ int32_t lmhead_dgrad_ws(const void *dlogits, int64_t ldd, const void *W, int64_t
 {
     LMH_TRY(check_dtype_out(dx_dtype));
     if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim || splits < 0 ||
-        splits > kMaxSplits || workspace_bytes < 0)
+        splits > kMaxSplits || workspace_bytes < 0 || !span_fits(M, K + 3, K + 3))
         return LMH_ERR_SHAPE;
     const int64_t need = 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
     if (need == 0)
@@ -590,7 +591,7 @@ int32_t lmhead_dgrad_noalloc(const void *dlogits, int64_t ldd, const void *W, in
 {
     LMH_TRY(check_dtype_out(dx_dtype));
     if (M < 0 || K < 0 || V < 0 || M > kMaxDim || K > kMaxDim || V > kMaxDim || splits < 0 ||
-        splits > kMaxSplits)
+        splits > kMaxSplits || !span_fits(M, K + 3, K + 3))
         return LMH_ERR_SHAPE;
     const int64_t need = 4 * lmh::dgrad_workspace_elems(M, K, V, splits);
     if (need == 0)
