@@ -30,6 +30,12 @@ def _say(*a):
     print(*a, flush=True)
 
 
+def _padded_ld(n, mult):
+    """A leading dimension past n (at least one element of padding) that is
+    a multiple of mult elements (the 16-byte row alignment the C ABI asks)."""
+    return (n + 2 * mult - 1) // mult * mult
+
+
 def _f32_bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
@@ -131,13 +137,99 @@ def test_logits_row_group_kernel_integer_exact(M, K, V, pad):
     assert padding_untouched(out) and padding_untouched(outb)
 
 
-def test_logits_k_zero_writes_zeros():
-    x = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
-    W = torch.empty((12, 0), dtype=torch.bfloat16, device="cuda")
-    out = torch.full((5, 12), float("nan"), device="cuda")
+@pytest.mark.parametrize("M,V", [
+    (5, 12),        # few tokens, 32-wide token tile
+    (48, 1000),     # few tokens, 64-wide token tile, ragged vocabulary
+    (300, 700),     # ring kernel, ragged both ways
+    (1024, 2048),   # ring kernel, whole 256 x 256 tiles
+])
+def test_logits_k_zero_writes_zeros(M, V):
+    """An empty contraction (K = 0) is the zero matrix: every kernel the
+    routing can pick stores zeros (FP32 and BF16) and leaves the padding of
+    the output rows alone."""
+    _say(f"logits K=0 M={M} V={V}")
+    x = torch.empty((M, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((V, 0), dtype=torch.bfloat16, device="cuda")
+    out = padded_out(M, V, _padded_ld(V, 4), torch.float32)
+    outb = padded_out(M, V, _padded_ld(V, 8), torch.bfloat16)
     lmh.lmhead_logits(x, W, out=out)
+    lmh.lmhead_logits(x, W, out=outb, out_dtype="bf16")
     torch.cuda.synchronize()
-    assert torch.all(out == 0).item()
+    assert not np.any(_f32_bits(host_f32(out)))
+    assert not np.any(host_bits(outb))
+    assert padding_untouched(out) and padding_untouched(outb)
+
+
+@pytest.mark.parametrize("M,V", [(100, 1000), (300, 700)])
+def test_logits_xent_k_zero_records(M, V):
+    """K = 0 with the records: the logits are all zero, so every record and
+    the merged statistics are those of a row of V equal logits (the loss of
+    a kept row is log V)."""
+    tgt = np.arange(M, dtype=np.int32) % V
+    tgt[1::5] = -100
+    _say(f"logits+records K=0 M={M} V={V}")
+    x = torch.empty((M, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((V, 0), dtype=torch.bfloat16, device="cuda")
+    t = torch.from_numpy(tgt).cuda()
+    out, part = lmh.lmhead_logits_xent(x, W, t)
+    loss, st = lmh.lmhead_xent_merge(part, t, V)
+    torch.cuda.synchronize()
+    z = np.zeros((M, V), dtype=np.float32)
+    assert not np.any(_f32_bits(host_f32(out)))
+    _check_records(host_f32(part), oracle.xent_partial(z, tgt, block_cols=256), "records")
+    ref = oracle.xent_fwd(z, tgt, -100)
+    lh = host_f32(loss)
+    keep = tgt != -100
+    assert np.all(np.abs(lh[keep] - np.log(V)) <= 1e-6 * np.log(V))
+    assert np.all(lh[~keep] == 0)
+    assert np.all(np.abs(host_f32(st)[:, 1] - ref[:, 1]) <= 1e-5 * ref[:, 1])
+
+
+@pytest.mark.parametrize("M,K", [
+    (16, 64),       # 128 x 128 tiles
+    (300, 700),     # ragged both ways
+    (2048, 8192),   # 256 x 256 tiles
+])
+def test_dgrad_v_zero_writes_zeros(M, K):
+    """V = 0: dX is the zero matrix for both output dtypes, through the
+    unsplit, split-request and no-alloc entry points (an empty sum has no
+    parts to split), padding untouched."""
+    _say(f"dgrad V=0 M={M} K={K}")
+    dl = torch.empty((M, 0), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    assert lmh.lmhead_dgrad_workspace_bytes(M, K, 0, 4) == 0
+    for dt, mult in ((torch.float32, 4), (torch.bfloat16, 8)):
+        for call in ("unsplit", "split", "noalloc"):
+            dX = padded_out(M, K, _padded_ld(K, mult), dt)
+            if call == "noalloc":
+                lmh.lmhead_dgrad_noalloc(dl, W, dX, splits=4)
+            else:
+                lmh.lmhead_dgrad(dl, W, dX=dX, splits=1 if call == "unsplit" else 4)
+            torch.cuda.synchronize()
+            assert not torch.any(dX != 0).item() and not torch.isnan(dX).any().item(), call
+            assert padding_untouched(dX), call
+
+
+@pytest.mark.parametrize("V,K", [
+    (1000, 64),     # 128 x 128 tiles
+    (4096, 2048),   # 256 x 128 tiles
+    (32768, 1024),  # two workgroups per CU
+])
+def test_wgrad_m_zero(V, K):
+    """M = 0: dW = 0 when storing; accumulating adds nothing and leaves dW
+    as it was."""
+    _say(f"wgrad M=0 V={V} K={K}")
+    dl = torch.empty((0, V), dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    dW = padded_out(V, K, _padded_ld(K, 4), torch.float32)
+    lmh.lmhead_wgrad(dl, x, dW=dW)
+    torch.cuda.synchronize()
+    assert not torch.any(dW != 0).item() and not torch.isnan(dW).any().item()
+    assert padding_untouched(dW)
+    dW.fill_(1.5)
+    lmh.lmhead_wgrad(dl, x, dW=dW, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.all(dW == 1.5).item()
 
 
 def test_logits_fp16_rejected():
