@@ -588,6 +588,9 @@ def test_split_merge_nan_rows():
                                       (600, 4097, "per_row"), (128, 32768, "scalar"),
                                       (5, 40001, "per_row"), (7, 65536, "scalar"),
                                       (3, 65537, "per_row"),
+                                      # one element either side of the whole-row forms
+                                      (4, 32767, "scalar"), (4, 32769, "per_row"),
+                                      (4, 65535, "scalar"),
                                       # several rounds of workgroups per CU
                                       (600, 32768, "per_row"), (520, 16384, "scalar"),
                                       (1024, 32768, "scalar")])
