@@ -1005,7 +1005,7 @@ gemm_big(GemmProblem gp, TileMap tm)
 // ---------------------------------------------------------------------------
 // gemm_small: the logits GEMM for few tokens (M <= 256), where the work is
 // bound by streaming W once from HBM.  Tiles of 128 vocabulary rows x BC
-// tokens (BC = 32, 64 or 128), 4 waves (each 32 rows x BC), BK = 64, and a
+// tokens (BC = 32, 64, 128 or 256), 4 waves (each 32 rows x BC), BK = 64, and a
 // ring of S LDS stages filled by direct buffer loads: S-1 stages are in
 // flight while one is consumed, which keeps enough bytes moving per CU to
 // approach the HBM rate.  The steady loop is unrolled S times so that every
@@ -2155,8 +2155,15 @@ hipError_t launch_gemm_logits(const GemmProblem &p, Epi epi, hipStream_t s)
     if (p.C <= 64)
         return p.P <= 4096 ? launch_small<64, 3, 128>(p, epi, 8, s)
                            : launch_small<64, 6>(p, epi, 8, s);
-    if (p.C <= 256)
+    if (p.C <= 128)
         return launch_small<128, LMH_SMALL_S128>(p, epi, 8, s);
+    // 129 - 256 tokens: one 256-token tile column (ring of 3 stages of 48
+    // KiB), so each W row block is streamed by one workgroup instead of two.
+    // Measured on MI355X against two 128-token columns (V=32768, FP32 out,
+    // medians of 40 alternated): M=256 K=1024 36.3 -> 30.4 us, K=4096 94.6
+    // -> 85.2, K=8192 204.4 -> 169.9; M=160 and 192 -6 to -17 %.
+    if (p.C <= 256)
+        return launch_small<256, 3>(p, epi, 8, s);
     // Many tokens: the ping-pong ring kernel for K <= 2048 or at most 384
     // tokens, gemm_big otherwise.  Measured on MI355X (V=32768, medians of 15,
     // three alternated rounds), gemm_pp -> gemm_big: M=1024 K=1024 79.6-80.6

@@ -92,6 +92,8 @@ def _up(v, m):
     # steady loop from 5 full stages on, ragged 128-deep tails (K = 1000)
     (40, 1024, 1000, 8), (64, 1000, 4100, 0), (64, 4096, 2049, 8), (40, 4096, 300, 16),
     (33, 1000, 777, 0), (16, 4096, 3000, 8), (64, 1024, 33, 0),
+    # 129 - 256 tokens: one 256-token tile column, a ring of 3 stages
+    (256, 1000, 1000, 8), (200, 4096, 2049, 0), (129, 640, 300, 16), (256, 8192, 513, 8),
 ])
 def test_logits_ragged_integer_exact(M, K, V, pad):
     """Ragged M, K, V (partial tiles on every edge, K not a multiple of the
