@@ -351,28 +351,27 @@ __global__ __launch_bounds__(WR * WC * 64) void gemm_kernel(GemmProblem g, TileM
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel for the logits GEMM, where both operands keep the
-// contraction dimension contiguous (W [V][K], x [M][K]).
-//
-// Workgroup tile BR x BC (R = vocabulary, C = tokens), WR x WC waves, each
-// wave owning a TR x TC block of 32x32 accumulators held in AGPRs (128 x 128
-// per wave: 256 accumulator registers, one wave per SIMD).  A larger wave
-// tile halves the LDS bytes read per MFMA compared with 64 x 64 wave tiles.
-// LDS holds [row][BK] BF16 with 16-byte chunks XOR-swizzled by row so that
-// both the staging writes and the MFMA fragment reads touch distinct banks
-// for any 8 (32-bank) or 16 (64-bank) consecutive lanes.  Global loads for
-// stage k+2 are issued as soon as stage k+1 has been written to LDS and
-// overlap the whole MFMA phase of stage k+1.
-// 256-byte rows (BK = 128, 16 chunks) take a 4-bit key, distinct over any 16
-// consecutive rows.
+// LDS stage layout of a contraction-contiguous operand (W [V][K], x [M][K],
+// dlogits [M][V] in dgrad): [row][BK] BF16, the 16-byte chunk c of row r kept
+// at chunk c ^ lds_swz(r).  An MFMA fragment read (ds_read_b128) has lane l
+// read row r0 + l % 32 at chunk (2 kk + l / 32) ^ lds_swz(row), and a direct
+// load writes 1 KiB linearly, so only the reads depend on the key.  Keys that
+// XOR the row's low bits with its higher bits ((r ^ r >> 3) & 7 for 128-byte
+// rows) leave those reads free of bank conflicts; the rotation
+// (r + (r >> 3)) & 7 used before cost ~4 stall cycles per read in the
+// persistent logits kernel (rocprofv3 SQ_LDS_BANK_CONFLICT: 50.3 M cycles
+// per launch at M=1024 K=8192 V=32768 -> 0, LDS busy cycles halved, the
+// launch 3 % shorter).  Over any 32-row aligned block the key is that of rows
+// 0 - 31 XOR a constant of the block, so every fragment reads as the first
+// does; for 128-byte rows the constant is 4 x (block parity).
 template <int BK>
 __device__ __forceinline__ int lds_swz(int row)
 {
     static_assert(BK == 64 || BK == 128, "swizzle defined for 128- and 256-byte rows");
     if constexpr (BK == 64)
-        return (row + (row >> 3)) & 7;
+        return (row ^ (row >> 3)) & 7;
     else
-        return (row + (row >> 4)) & 15;
+        return (row ^ (row >> 4)) & 15;
 }
 
 __device__ __forceinline__ void lds_barrier()
