@@ -48,6 +48,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;
 
@@ -1725,9 +1726,11 @@ hipError_t launch_wg2(const GemmProblem &p, Epi epi, int group_r, hipStream_t s)
 //    stores, and the other four waves' stores never hold up a stage.
 // Stage s of a tile sits in LDS buffer s % 2 (the stage count is even, so
 // every tile starts in buffer 0).  Loads are issued from inline assembly,
-// untracked by the compiler; the waits count them exactly.  Same operand
-// layouts, MFMA order and accumulation order as gemm_big's 256 x 256 tile, so
-// the two give bitwise-identical output.
+// untracked by the compiler; the waits count them exactly.  In its 32 x 32 x
+// 16 form (wgrad, and the logits GEMM below 1024 tokens) the operand layouts,
+// MFMA order and accumulation order are gemm_big's 256 x 256 tile's, so the
+// two give bitwise-identical output; the logits GEMM from 1024 tokens on runs
+// the 16 x 16 x 32 form (MF16), which sums each output in another order.
 __device__ __forceinline__ int persist_swz(int row)
 {
     // 16-byte chunk key of a 128-byte row: distinct over any 8 consecutive
@@ -1735,7 +1738,7 @@ __device__ __forceinline__ int persist_swz(int row)
     return (row & 7) ^ ((row >> 3) & 1);
 }
 
-template <bool TRANS, int EPI>
+template <bool TRANS, int EPI, bool MF16>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_persist(GemmProblem g, TileMap tm, int per_xcd)
 {
@@ -1750,6 +1753,9 @@ gemm_persist(GemmProblem g, TileMap tm, int per_xcd)
     using OpB = std::conditional_t<TRANS, TrOperand<BC, BK, NL>, DmaOperand<BC, BK, NL>>;
     constexpr int NDMA = OpA::NB + OpB::NB;    // direct loads per loading wave per stage
     constexpr int NST = FR * FC * (BF ? 2 : 4);  // stores per wave per tile
+    // MF16: the 16 x 16 x 32 MFMA form (contraction-contiguous operands only);
+    // its epilogue issues the same NST stores per wave per tile.
+    static_assert(!(MF16 && TRANS), "the 16 x 16 form reads k-contiguous stages");
     __shared__ __attribute__((aligned(16))) uint16_t sA0[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[BR * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sB0[BC * BK];
@@ -1932,6 +1938,232 @@ gemm_persist(GemmProblem g, TileMap tm, int per_xcd)
             }
     };
 
+    if constexpr (MF16) {
+        // 16 x 16 x 32 form.  Fragment i of A covers wave rows 16 i .. 16 i + 15
+        // (lane l: row l % 16, the 8 contraction values from 8 (l / 16) of the
+        // 32-wide k step), fragment jj of B the tokens 16 jj .. 16 jj + 15; lane l
+        // then holds outputs (rows 16 i + 4 (l / 16) .. + 3, token 16 jj + l % 16).
+        // A 64-deep stage is two k steps of 4 x 8 MFMAs.  Each fragment
+        // register is reloaded for the next k step as soon as its last MFMA of
+        // the current one is issued (A: after its row, B: after the last row),
+        // so one set of fragment registers suffices; the next stage's first
+        // fragments are read behind the hand-off, which sits after the first
+        // three rows of k step 1 (after two it measured 1 - 5 % slower).  Against the 32 x 32 x 16 form the matrix pipe
+        // moves half the accumulator bytes per FLOP, which at the board's power
+        // cap buys clock.
+        constexpr int GR = TR / 16, GC = TC / 16;
+        const int q16 = lane >> 4, t16 = lane & 15;
+        const int rA = wr * TR + t16, rB = wc * TC + t16;
+        // Stage rows here take the key r % 8 (chunk c of row r at c ^ (r % 8)),
+        // not lds_swz: a fragment read of this form (16 rows x 4 chunks) is
+        // free of bank conflicts with it and conflicts with lds_swz's XOR key
+        // (measured: 50 M conflict cycles per launch at M=1024 K=8192).  The
+        // key of every fragment row is t16 % 8, so one per-lane term serves all.
+        const int v16 = q16 ^ (t16 & 7);
+        bf16x8 ga[GR], gb[GC];
+        f32x4 acc4[GR][GC];
+        auto ldA = [&](const uint16_t *l, int i, int h) {
+            ga[i] = *reinterpret_cast<const bf16x8 *>(&l[(rA + 16 * i) * BK + ((v16 ^ (4 * h)) << 3)]);
+        };
+        auto ldB = [&](const uint16_t *l, int jj, int h) {
+            gb[jj] = *reinterpret_cast<const bf16x8 *>(&l[(rB + 16 * jj) * BK + ((v16 ^ (4 * h)) << 3)]);
+        };
+        auto mf = [&](int i, int jj) {
+            acc4[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[i], gb[jj], acc4[i][jj], 0, 0, 0);
+        };
+        // k step 0 of the stage in (cA, cB), reloading for its k step 1.
+        auto step0 = [&](const uint16_t *cA, const uint16_t *cB) {
+#pragma unroll
+            for (int i = 0; i < GR; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < GC; ++jj) {
+                    mf(i, jj);
+                    if (i == GR - 1)
+                        ldB(cB, jj, 1);
+                }
+                ldA(cA, i, 1);
+            }
+        };
+        constexpr int HEAD = GR - 1;  // rows of k step 1 before the hand-off
+        auto step1_head = [&]() {
+#pragma unroll
+            for (int i = 0; i < HEAD; ++i)
+#pragma unroll
+                for (int jj = 0; jj < GC; ++jj)
+                    mf(i, jj);
+        };
+        // The rest of k step 1, loading k step 0 of the next stage (nA, nB)
+        // when NEXT (the last stage of a tile has none).
+        auto step1_tail = [&](auto nextc, const uint16_t *nA, const uint16_t *nB) {
+            constexpr bool NEXT = decltype(nextc)::value;
+            if constexpr (NEXT) {
+#pragma unroll
+                for (int i = 0; i < HEAD; ++i)
+                    ldA(nA, i, 0);
+            }
+#pragma unroll
+            for (int i = HEAD; i < GR; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < GC; ++jj) {
+                    mf(i, jj);
+                    if constexpr (NEXT)
+                        if (i == GR - 1)
+                            ldB(nB, jj, 0);
+                }
+                if constexpr (NEXT)
+                    ldA(nA, i, 0);
+            }
+        };
+        // Each wave writes its 64 x 128 block through its 4 KiB LDS area, 16
+        // tokens at a time: FP32 rows of 256 bytes (16-byte chunk k of row t at
+        // k ^ t, four rows per store instruction), BF16 rows of 128 bytes
+        // (chunk k at k ^ (t % 8), eight rows per store): NST stores per tile.
+        char *const ownb = reinterpret_cast<char *>(sE + wave * 32 * 32);
+        auto epilogue16 = [&](int64_t r0, int64_t c0) {
+#pragma unroll
+            for (int jj = 0; jj < GC; ++jj) {
+                if constexpr (BF) {
+#pragma unroll
+                    for (int i = 0; i < GR; ++i) {
+                        const f32x2 lo = {acc4[i][jj][0], acc4[i][jj][1]};
+                        const f32x2 hi = {acc4[i][jj][2], acc4[i][jj][3]};
+                        uint2 w;
+                        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+                        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+                        *reinterpret_cast<uint2 *>(ownb + t16 * 128 +
+                                                   (((2 * i + (q16 >> 1)) ^ (t16 & 7)) << 4) +
+                                                   (q16 & 1) * 8) = w;
+                    }
+#pragma unroll
+                    for (int sx = 0; sx < 2; ++sx) {
+                        const int rr = 8 * sx + (lane >> 3), kc = lane & 7;
+                        const uint4 v = *reinterpret_cast<const uint4 *>(
+                            ownb + rr * 128 + ((kc ^ (rr & 7)) << 4));
+                        uint16_t *out = static_cast<uint16_t *>(g.D) +
+                                        (c0 + wc * TC + 16 * jj + rr) * g.ldd + r0 + wr * TR + 8 * kc;
+                        store16(out, v, true);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < GR; ++i) {
+                        float4 v;
+                        v.x = acc4[i][jj][0];
+                        v.y = acc4[i][jj][1];
+                        v.z = acc4[i][jj][2];
+                        v.w = acc4[i][jj][3];
+                        *reinterpret_cast<float4 *>(ownb + t16 * 256 + (((4 * i + q16) ^ t16) << 4)) = v;
+                    }
+#pragma unroll
+                    for (int sx = 0; sx < 4; ++sx) {
+                        const int rr = 4 * sx + q16, kc = t16;
+                        const float4 v = *reinterpret_cast<const float4 *>(
+                            ownb + rr * 256 + ((kc ^ rr) << 4));
+                        float *out = static_cast<float *>(g.D) +
+                                     (c0 + wc * TC + 16 * jj + rr) * g.ldd + r0 + wr * TR + 4 * kc;
+                        store16(out, v, true);
+                    }
+                }
+            }
+        };
+        static_assert(GC * (BF ? 2 : 4) == NST, "the 16 x 16 epilogue issues NST stores");
+        // Direct loads as DmaOperand's, with the key above and the offsets
+        // recomputed per load rather than held in registers: block b (8 rows)
+        // of a stage, lane l at row 8 b + l / 8, chunk (l % 8) ^ (l / 8).
+        const int dl_row = lane >> 3, dl_key = (lane & 7) ^ dl_row;
+        auto dma16 = [&](uint16_t *lA, uint16_t *lB, int64_t r0, int64_t c0, int64_t kt) {
+            if (!loads)
+                return;
+            const __amdgpu_buffer_rsrc_t ra = tile_rsrc(g.A + r0 * g.lda);
+            const __amdgpu_buffer_rsrc_t rb = tile_rsrc(g.B + c0 * g.ldb);
+            const int soff = static_cast<int>(kt * BK * 2);
+#pragma unroll
+            for (int i = 0; i < OpA::NB; ++i) {
+                const int b = wr * OpA::NB + i;
+                const uint32_t voff =
+                    static_cast<uint32_t>(((b * 8 + dl_row) * g.lda + (dl_key << 3)) * 2);
+                dma16_untracked(ra, lds_addr(lA + b * 512), voff, soff);
+            }
+#pragma unroll
+            for (int i = 0; i < OpB::NB; ++i) {
+                const int b = wr * OpB::NB + i;
+                const uint32_t voff =
+                    static_cast<uint32_t>(((b * 8 + dl_row) * g.ldb + (dl_key << 3)) * 2);
+                dma16_untracked(rb, lds_addr(lB + b * 512), voff, soff);
+            }
+        };
+
+        const int64_t nk = g.P / BK;  // even, >= 2
+        int j = blockIdx.x / kXcds;
+        if (j >= per_xcd)
+            return;
+        int64_t r0, c0;
+        decode(j, r0, c0);
+        dma16(sA0, sB0, r0, c0, 0);
+        dma16(sA1, sB1, r0, c0, 1);
+        bool first = true;
+        const std::true_type with_next;
+        const std::false_type no_next;
+        for (;;) {
+            const std::integral_constant<int, NDMA> after_s0_first;
+            const std::integral_constant<int, NDMA + NST> after_s0;
+            if (first)
+                hand_off(after_s0_first);
+            else
+                hand_off(after_s0);
+#pragma unroll
+            for (int i = 0; i < GR; ++i)
+#pragma unroll
+                for (int jj = 0; jj < GC; ++jj)
+                    acc4[i][jj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < GR; ++i)
+                ldA(sA0, i, 0);
+#pragma unroll
+            for (int jj = 0; jj < GC; ++jj)
+                ldB(sB0, jj, 0);
+            const int jn = j + slots;
+            const bool has_next = jn < per_xcd;
+            int64_t nr0 = 0, nc0 = 0;
+            if (has_next)
+                decode(jn, nr0, nc0);
+            step0(sA0, sB0);
+            step1_head();
+            const std::integral_constant<int, 0> none;
+            const std::integral_constant<int, NST> after_s1;
+            if (first)
+                hand_off(none);
+            else
+                hand_off(after_s1);
+            step1_tail(with_next, sA1, sB1);
+            int64_t kt = 1;
+            for (; kt + 2 < nk; kt += 2) {
+                dma16(sA0, sB0, r0, c0, kt + 1);
+                step0(sA1, sB1);
+                step1_head();
+                hand_off(none);
+                step1_tail(with_next, sA0, sB0);
+                dma16(sA1, sB1, r0, c0, kt + 2);
+                step0(sA0, sB0);
+                step1_head();
+                hand_off(none);
+                step1_tail(with_next, sA1, sB1);
+            }
+            if (has_next)
+                dma16(sA0, sB0, nr0, nc0, 0);
+            step0(sA1, sB1);
+            step1_head();
+            step1_tail(no_next, nullptr, nullptr);
+            pp_barrier();
+            if (has_next)
+                dma16(sA1, sB1, nr0, nc0, 1);
+            epilogue16(r0, c0);
+            if (!has_next)
+                break;
+            j = jn, r0 = nr0, c0 = nc0;
+            first = false;
+        }
+        return;
+    }
     const int64_t nk = g.P / BK;  // even, >= 2
     int j = blockIdx.x / kXcds;
     if (j >= per_xcd)
@@ -2023,13 +2255,36 @@ hipError_t launch_persist(const GemmProblem &p, Epi epi, int group_r, hipStream_
     tm.tiles_c = static_cast<int>(p.C / 256);
     tm.group_r = std::min(std::max(group_r, 1), tm.tiles_r);
     const int per_xcd = tm.tiles_r * tm.tiles_c / kXcds;
+    // The logits GEMM takes the 16 x 16 x 32 form from 1024 tokens on.
+    // Measured on MI355X against the 32 x 32 x 16 form (same box; alternated
+    // calls / 2 s back to back at the 1400 W cap): M=1024 K=8192 V=32768
+    // 445 -> 419 us / 1234 -> 1330 TFLOPS, M=4096 K=8192 1732 -> 1661 us,
+    // M=1024 K=16384 870 -> 855 us; but M=512 K=16384 V=131072 1883 -> 2163 us
+    // (1180 -> 986 TFLOPS at a higher clock) and M=512 K=8192 V=65536 +5 %.
+#ifndef LMH_MF16_MIN_TOKENS
+#define LMH_MF16_MIN_TOKENS 1024
+#endif
+    const bool mf16 = !TRANS && p.C >= LMH_MF16_MIN_TOKENS;
     // One workgroup per CU (160 KiB of LDS each).
-    if (epi == Epi::kStoreF32)
-        hipLaunchKernelGGL((gemm_persist<TRANS, 0>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
-    else if (epi == Epi::kStoreBF16)
-        hipLaunchKernelGGL((gemm_persist<TRANS, 1>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
-    else
+    if (epi == Epi::kStoreF32) {
+        if constexpr (!TRANS) {
+            if (mf16) {
+                hipLaunchKernelGGL((gemm_persist<TRANS, 0, true>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((gemm_persist<TRANS, 0, false>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+    } else if (epi == Epi::kStoreBF16) {
+        if constexpr (!TRANS) {
+            if (mf16) {
+                hipLaunchKernelGGL((gemm_persist<TRANS, 1, true>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((gemm_persist<TRANS, 1, false>), dim3(256), dim3(512), 0, s, p, tm, per_xcd);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
