@@ -1948,9 +1948,9 @@ gemm_persist(GemmProblem g, TileMap tm, int per_xcd)
         // the current one is issued (A: after its row, B: after the last row),
         // so one set of fragment registers suffices; the next stage's first
         // fragments are read behind the hand-off, which sits after the first
-        // three rows of k step 1 (after two it measured 1 - 5 % slower).  Against the 32 x 32 x 16 form the matrix pipe
-        // moves half the accumulator bytes per FLOP, which at the board's power
-        // cap buys clock.
+        // three rows of k step 1 (after two it measured 1 - 5 % slower).
+        // Against the 32 x 32 x 16 form the matrix pipe moves half the
+        // accumulator bytes per FLOP, which at the board's power cap buys clock.
         constexpr int GR = TR / 16, GC = TC / 16;
         const int q16 = lane >> 4, t16 = lane & 15;
         const int rA = wr * TR + t16, rB = wc * TC + t16;
